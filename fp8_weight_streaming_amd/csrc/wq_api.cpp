@@ -1,0 +1,368 @@
+// wq_api.cpp -- host side of libwq: argument validation, K-split planning,
+// workspace layout and the launches behind the C ABI in include/wq.h.
+//
+// Validation never touches the HIP runtime, so every argument error is
+// reported without a device (and with nothing enqueued).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "wq.h"
+#include "wq_internal.h"
+
+namespace wq {
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- device facts, cached per device ---------------------------------------
+struct DeviceInfo {
+  bool probed = false;
+  bool ok = false;
+  int cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Returns the CU count of the current device, or 0 if there is no usable
+// gfx950 device.
+int current_cus() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.probed) {
+    d.probed = true;
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess && std::strncmp(p.gcnArchName, "gfx950", 6) == 0 &&
+        p.multiProcessorCount > 0) {
+      d.ok = true;
+      d.cus = p.multiProcessorCount;
+    }
+  }
+  return d.ok ? d.cus : 0;
+}
+
+// ---- K-split plan ------------------------------------------------------------
+struct Split {
+  int kc = 0;
+  int nchunks = 0;
+  int ntiles = 0;
+};
+
+int seg_k(int fmt) { return fmt == kFmtNvfp4 ? 128 : 64; }
+
+Split make_split(int fmt, int M, int K, int kc) {
+  Split s;
+  s.kc = kc;
+  s.nchunks = (int)ceil_div(K, kc);
+  s.ntiles = (int)ceil_div(M, 16);
+  return s;
+}
+
+// In a verify pass many matrices share the machine, so K is split only as
+// far as the LDS budget requires.
+Split verify_split(int fmt, int M, int K) {
+  const int sk = seg_k(fmt);
+  const int n = (int)ceil_div(K, kKcMax);
+  const int kc = (int)(ceil_div(ceil_div(K, n), sk) * sk);
+  return make_split(fmt, M, K, kc);
+}
+
+// A single product may split K further so that every wave of every CU has
+// a unit of work.  Candidate splits are scored by the work of the busiest
+// wave: rounds of units times (segments per unit + a ramp of kPrefetch
+// segments); a split must save at least 10% over the next-coarser best to
+// be taken, since it costs partial-sum traffic.
+Split gemm_split(int fmt, int M, int K, int cus) {
+  const int sk = seg_k(fmt);
+  const int64_t slots = (int64_t)cus * kWaves;
+  const int64_t ntiles = ceil_div(M, 16);
+  const int nmin = (int)ceil_div(K, kKcMax);
+  const int nmax = std::max(nmin, (int)std::min<int64_t>(64, ceil_div(K, sk)));
+  Split best = verify_split(fmt, M, K);
+  double best_cost = 1e300;
+  for (int n = nmin; n <= nmax; ++n) {
+    const int kc = (int)(ceil_div(ceil_div(K, n), sk) * sk);
+    const int nc = (int)ceil_div(K, kc);
+    if (nc != n && n != nmin) continue;  // this n rounds to a split already scored
+    const int64_t units = ntiles * nc;
+    const int64_t rounds = ceil_div(units, slots);
+    const double cost = (double)rounds * ((double)(kc / sk) + kPrefetch);
+    if (cost < 0.9 * best_cost) {
+      best_cost = cost;
+      best = make_split(fmt, M, K, kc);
+    }
+  }
+  return best;
+}
+
+// ---- validation ------------------------------------------------------------------
+wq_status check_shape(int fmt, int M, int K, int N) {
+  if (fmt != kFmtNvfp4 && fmt != kFmtFp8Row) return WQ_ERROR_INVALID_VALUE;
+  if (N < 1 || N > 8 || M < 1 || K < 1) return WQ_ERROR_INVALID_VALUE;
+  const int mult = fmt == kFmtNvfp4 ? 32 : 16;
+  if (K % mult != 0 || K > (1 << 24)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  const uint64_t wbytes = fmt == kFmtNvfp4 ? (uint64_t)M * (uint64_t)(K / 2) : (uint64_t)M * (uint64_t)K;
+  if (wbytes >= (1ull << 40)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  return WQ_SUCCESS;
+}
+
+wq_status check_ptrs(const void* w, const void* s, const void* x, const void* y) {
+  if (!w || !s || !x || !y) return WQ_ERROR_INVALID_VALUE;
+  if (!aligned16(w) || !aligned16(s) || !aligned16(x) || !aligned16(y)) return WQ_ERROR_MISALIGNED;
+  return WQ_SUCCESS;
+}
+
+// Workspace bytes of the split-K scratch of one matrix.
+size_t split_scratch_bytes(const Split& s, int M, int N) {
+  if (s.nchunks <= 1) return 0;
+  return align_up((size_t)s.nchunks * N * M * sizeof(float), kAlign) +
+         align_up((size_t)s.ntiles * sizeof(unsigned), kAlign);
+}
+
+DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x, float* y, int M, int K,
+               const Split& sp, char* scratch, int N, int64_t unit0) {
+  DevMat d{};
+  d.w = static_cast<const uint8_t*>(w);
+  d.s = fmt == kFmtNvfp4 ? static_cast<const uint8_t*>(s) : nullptr;
+  d.rs = fmt == kFmtFp8Row ? static_cast<const float*>(s) : nullptr;
+  d.x = x;
+  d.y = y;
+  d.g = g;
+  d.fmt = fmt;
+  d.M = M;
+  d.K = K;
+  d.kc = sp.kc;
+  d.nchunks = sp.nchunks;
+  d.ntiles = sp.ntiles;
+  d.unit0 = unit0;
+  if (sp.nchunks > 1) {
+    d.part = reinterpret_cast<float*>(scratch);
+    d.cnt = reinterpret_cast<unsigned*>(scratch + align_up((size_t)sp.nchunks * N * M * sizeof(float), kAlign));
+  }
+  return d;
+}
+
+wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x, float* y, int M, int K,
+               int N, void* ws, size_t ws_bytes, void* stream) {
+  wq_status st = check_shape(fmt, M, K, N);
+  if (st != WQ_SUCCESS) return st;
+  st = check_ptrs(w, s, x, y);
+  if (st != WQ_SUCCESS) return st;
+  if (ws && !aligned16(ws)) return WQ_ERROR_MISALIGNED;
+  const int cus = current_cus();
+  if (cus <= 0) return WQ_ERROR_DEVICE;
+  const Split sp = gemm_split(fmt, M, K, cus);
+  const size_t need = split_scratch_bytes(sp, M, N);
+  if (need > 0 && (!ws || ws_bytes < need)) return WQ_ERROR_WORKSPACE;
+  const DevMat one = dev_mat(fmt, w, s, g, x, y, M, K, sp, static_cast<char*>(ws), N, 0);
+  const int64_t units = (int64_t)sp.nchunks * sp.ntiles;
+  const int grid = (int)std::min<int64_t>(cus, units);
+  const int mode = fmt == kFmtFp8Row ? kModeFp8 : (K % 64 == 0 ? kModeNvfp4Aligned : kModeNvfp4);
+  const hipError_t e = launch_stream(N, mode, nullptr, nullptr, one, grid, lds_bytes_for(N),
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+// ---- verify pass layout ------------------------------------------------------
+struct PassLayout {
+  std::vector<Split> splits;
+  std::vector<size_t> scratch_off;
+  size_t table_bytes = 0, ranges_bytes = 0, scratch_bytes = 0, total = 0;
+  int grid = 0;
+  int64_t units = 0;
+};
+
+wq_status check_descs(const wq_matrix* descs, int count, int N) {
+  if (!descs || count < 1 || N < 1 || N > 8) return WQ_ERROR_INVALID_VALUE;
+  for (int i = 0; i < count; ++i) {
+    const wq_matrix& d = descs[i];
+    wq_status st = check_shape(d.fmt, d.M, d.K, N);
+    if (st != WQ_SUCCESS) return st;
+    st = check_ptrs(d.w, d.scales, d.x, d.y);
+    if (st != WQ_SUCCESS) return st;
+  }
+  return WQ_SUCCESS;
+}
+
+PassLayout pass_layout(const wq_matrix* descs, int count, int N, int cus) {
+  PassLayout L;
+  L.splits.resize(count);
+  L.scratch_off.resize(count);
+  for (int i = 0; i < count; ++i) {
+    L.splits[i] = verify_split(descs[i].fmt, descs[i].M, descs[i].K);
+    L.units += (int64_t)L.splits[i].nchunks * L.splits[i].ntiles;
+  }
+  L.grid = (int)std::min<int64_t>(cus, L.units);
+  L.table_bytes = align_up((size_t)count * sizeof(DevMat), kAlign);
+  L.ranges_bytes = align_up((size_t)(L.grid + 1) * sizeof(WgRange), kAlign);
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    L.scratch_off[i] = off;
+    off += split_scratch_bytes(L.splits[i], descs[i].M, N);
+  }
+  L.scratch_bytes = off;
+  L.total = L.table_bytes + L.ranges_bytes + L.scratch_bytes;
+  return L;
+}
+
+// Splits the unit list into grid runs of (nearly) equal cost, where a
+// unit's cost is the weight bytes of its 16 rows in its K chunk plus a fixed
+// per-unit overhead.  Units of one (matrix, chunk) cost the same, so each
+// boundary inside such a group is found by division.
+std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout& L) {
+  auto unit_cost = [&](int i, int c) {
+    const Split& sp = L.splits[i];
+    const int klen = std::min(sp.kc, descs[i].K - c * sp.kc);
+    const double bytes_per_k = descs[i].fmt == kFmtNvfp4 ? 16.0 * 0.5625 : 16.0;
+    return bytes_per_k * klen + 4096.0;
+  };
+  double total = 0.0;
+  for (int i = 0; i < count; ++i)
+    for (int c = 0; c < L.splits[i].nchunks; ++c) total += unit_cost(i, c) * L.splits[i].ntiles;
+  std::vector<WgRange> ranges(L.grid + 1, WgRange{0, 0, 0});
+  int w = 1;
+  double acc = 0.0;
+  int64_t u = 0;
+  for (int i = 0; i < count; ++i) {
+    const Split& sp = L.splits[i];
+    for (int c = 0; c < sp.nchunks; ++c) {
+      const double uc = unit_cost(i, c);
+      const double end = acc + uc * sp.ntiles;
+      while (w < L.grid && total * w / L.grid < end) {
+        const double need = (total * w / L.grid - acc) / uc;
+        int64_t j = need <= 0.0 ? 0 : (int64_t)std::ceil(need);
+        if (j > sp.ntiles) j = sp.ntiles;
+        ranges[w] = WgRange{u + j, i, 0};
+        ++w;
+      }
+      acc = end;
+      u += sp.ntiles;
+    }
+  }
+  for (; w <= L.grid; ++w) ranges[w] = WgRange{L.units, count - 1, 0};
+  ranges[0] = WgRange{0, 0, 0};
+  return ranges;
+}
+
+}  // namespace
+}  // namespace wq
+
+using namespace wq;
+
+extern "C" {
+
+const char* wq_status_string(wq_status s) {
+  switch (s) {
+    case WQ_SUCCESS: return "success";
+    case WQ_ERROR_INVALID_VALUE: return "invalid value";
+    case WQ_ERROR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case WQ_ERROR_MISALIGNED: return "misaligned pointer";
+    case WQ_ERROR_WORKSPACE: return "workspace missing or too small";
+    case WQ_ERROR_LAUNCH: return "launch failed";
+    case WQ_ERROR_DEVICE: return "no usable gfx950 device";
+  }
+  return "unknown status";
+}
+
+size_t wq_gemm_workspace_bytes(int fmt, int M, int K, int N) {
+  if (check_shape(fmt, M, K, N) != WQ_SUCCESS) return 0;
+  const int cus = current_cus();
+  if (cus <= 0) return 0;
+  return split_scratch_bytes(gemm_split(fmt, M, K, cus), M, N);
+}
+
+wq_status wq_gemm_split(int fmt, int M, int K, int in_verify_pass, int* k_chunk, int* n_chunks) {
+  if (!k_chunk || !n_chunks) return WQ_ERROR_INVALID_VALUE;
+  wq_status st = check_shape(fmt, M, K, 1);
+  if (st != WQ_SUCCESS) return st;
+  Split sp;
+  if (in_verify_pass) {
+    sp = verify_split(fmt, M, K);
+  } else {
+    const int cus = current_cus();
+    if (cus <= 0) return WQ_ERROR_DEVICE;
+    sp = gemm_split(fmt, M, K, cus);
+  }
+  *k_chunk = sp.kc;
+  *n_chunks = sp.nchunks;
+  return WQ_SUCCESS;
+}
+
+wq_status wq_gemm_nvfp4(const uint8_t* codes, const uint8_t* scales, float global_scale, const uint16_t* x,
+                        float* y, int M, int K, int N, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm(kFmtNvfp4, codes, scales, global_scale, x, y, M, K, N, workspace, workspace_bytes, stream);
+}
+
+wq_status wq_gemm_fp8row(const uint8_t* w, const float* row_scale, const uint16_t* x, float* y, int M, int K,
+                         int N, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm(kFmtFp8Row, w, row_scale, 1.0f, x, y, M, K, N, workspace, workspace_bytes, stream);
+}
+
+size_t wq_verify_workspace_bytes(const wq_matrix* descs, int count, int N) {
+  if (check_descs(descs, count, N) != WQ_SUCCESS) return 0;
+  const int cus = current_cus();
+  if (cus <= 0) return 0;
+  return pass_layout(descs, count, N, cus).total;
+}
+
+wq_status wq_verify_pass(const wq_matrix* descs, int count, int N, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  wq_status st = check_descs(descs, count, N);
+  if (st != WQ_SUCCESS) return st;
+  if (!workspace) return WQ_ERROR_WORKSPACE;
+  if (!aligned16(workspace)) return WQ_ERROR_MISALIGNED;
+  const int cus = current_cus();
+  if (cus <= 0) return WQ_ERROR_DEVICE;
+  const PassLayout L = pass_layout(descs, count, N, cus);
+  if (workspace_bytes < L.total) return WQ_ERROR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  char* scratch = ws + L.table_bytes + L.ranges_bytes;
+
+  // host staging of the table and the ranges; thread-local so concurrent
+  // calls on different threads do not share it
+  thread_local std::vector<char> host;
+  host.assign(L.table_bytes + L.ranges_bytes, 0);
+  std::vector<DevMat> mats(count);
+  int64_t unit0 = 0;
+  for (int i = 0; i < count; ++i) {
+    const wq_matrix& d = descs[i];
+    mats[i] = dev_mat(d.fmt, d.w, d.scales, d.global_scale, d.x, d.y, d.M, d.K, L.splits[i],
+                      scratch + L.scratch_off[i], N, unit0);
+    unit0 += (int64_t)L.splits[i].nchunks * L.splits[i].ntiles;
+  }
+  const std::vector<WgRange> ranges = balance(descs, count, L);
+  std::memcpy(host.data(), mats.data(), sizeof(DevMat) * count);
+  std::memcpy(host.data() + L.table_bytes, ranges.data(), sizeof(WgRange) * ranges.size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+    return WQ_ERROR_LAUNCH;
+  bool any_nv = false, any_fp8 = false, all_aligned = true;
+  for (int i = 0; i < count; ++i) {
+    if (descs[i].fmt == kFmtNvfp4) {
+      any_nv = true;
+      all_aligned = all_aligned && descs[i].K % 64 == 0;
+    } else {
+      any_fp8 = true;
+    }
+  }
+  const int mode = any_nv && any_fp8 ? kModeMixed : any_fp8 ? kModeFp8 : all_aligned ? kModeNvfp4Aligned : kModeNvfp4;
+  const DevMat none{};
+  const hipError_t e = launch_stream(N, mode, reinterpret_cast<const DevMat*>(ws),
+                                     reinterpret_cast<const WgRange*>(ws + L.table_bytes), none, L.grid,
+                                     lds_bytes_for(N), s);
+  return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// wq_internal.h -- device-side descriptors and launch constants shared by
+// the host planner (wq_api.cpp) and the kernels (wq_kernels.hip).
+#ifndef WQ_INTERNAL_H
+#define WQ_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+constexpr int kFmtNvfp4 = 0;
+constexpr int kFmtFp8Row = 1;
+
+// One persistent workgroup per CU: 16 waves of 64 lanes.
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+// Segments (64 bytes of one row per lane group of four lanes) in flight.
+constexpr int kPrefetch = 8;
+// Shallower pipeline for the variants that also carry unaligned-scale or
+// mixed-format code, to stay within 128 VGPRs.
+constexpr int kPrefetchGeneric = 4;
+// Largest K chunk whose N <= 8 BF16 columns are staged in LDS at once.
+constexpr int kKcMax = 8704;
+// LDS: X chunk as (k/8, n) pieces of 16 bytes, then a zero block read by the
+// lanes whose A-operand slots are structurally zero.
+template <int N>
+__host__ __device__ constexpr uint32_t kZeroOffset() { return (uint32_t)kKcMax * 2u * N; }
+template <int N>
+__host__ __device__ constexpr uint32_t kZeroBytes() { return 256u * N; }
+constexpr uint32_t lds_bytes_for(int n) { return (uint32_t)kKcMax * 2u * n + 256u * n; }
+constexpr uint32_t kMaxLdsBytes = lds_bytes_for(8);
+
+// Device-side descriptor of one matrix (built on the host).
+struct DevMat {
+  const uint8_t* w;   // NVFP4 codes [M][K/2] or FP8 codes [M][K]
+  const uint8_t* s;   // NVFP4 block scales [M][K/16] (null for FP8-row)
+  const float* rs;    // FP8 row scales [M] (null for NVFP4)
+  const uint16_t* x;  // BF16 [N][K]
+  float* y;           // FP32 [N][M]
+  float* part;        // split-K partial sums [nchunks][N][M] (null if nchunks == 1)
+  unsigned* cnt;      // split-K arrival counters [ntiles] (null if nchunks == 1)
+  float g;            // NVFP4 per-tensor scale
+  int fmt, M, K;
+  int kc;             // K chunk length (multiple of the format's segment)
+  int nchunks;
+  int ntiles;         // ceil(M / 16)
+  int64_t unit0;      // index of this matrix's first unit in the pass
+};
+
+// First unit (and the matrix holding it) of each workgroup's run.
+struct WgRange {
+  int64_t begin;
+  int32_t mat;
+  int32_t pad;
+};
+
+// Kernel variants: which unit bodies a launch contains.
+constexpr int kModeNvfp4Aligned = 0;  // NVFP4 only, K % 64 == 0 for every matrix
+constexpr int kModeNvfp4 = 1;         // NVFP4 only, any K % 32 == 0
+constexpr int kModeFp8 = 2;           // FP8-row only
+constexpr int kModeMixed = 3;         // both formats
+
+hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
+                         int grid, size_t lds_bytes, hipStream_t stream);
+
+}  // namespace wq
+
+#endif

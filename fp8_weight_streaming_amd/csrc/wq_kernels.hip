@@ -1,0 +1,419 @@
+// wq_kernels.hip -- gfx950 kernels of the verify-pass skinny GEMM
+//     Y[n][m] = sum_k W[m][k] * X[n][k],  N <= 8 columns,
+// for W in NVFP4 (E2M1 codes, one E4M3 scale per 16 k, FP32 tensor scale)
+// or in row-scaled FP8-E4M3, X in BF16, Y in FP32.
+//
+// The crit-hub engine card "mtp7-device-confidence" (section "Design", row
+// "GEMVs") runs this product on an RTX 5090 by reading the weight bytes
+// straight into BF16 tensor-core fragments.  What is kept here: weights are
+// read once, in their stored bytes, and widened to BF16 only in registers.
+// What is rebuilt for CDNA4 (one 1024-thread workgroup per CU, wave64):
+//
+//  * One wave owns a tile of 16 weight rows and walks its K range in
+//    segments of 64 bytes per row (one 16-byte buffer load per lane, four
+//    lanes per row), PF segments in flight.
+//  * E2M1 -> BF16 and E4M3 -> BF16 use gfx950's scaled conversion
+//    instructions with scale 1.0, which are exact.  Those instructions
+//    apply only the exponent of their scale, so an E4M3 block scale (which
+//    has mantissa bits) cannot ride on them.  Instead the NVFP4 path puts
+//    the two 16-k scale blocks of a 32-k MFMA step on different A rows:
+//    A = X arranged as 16 rows (block b, column n), zero where the k slot
+//    belongs to the other block, B = the 16 weight rows' codes.  The
+//    16x16x32 BF16 MFMA then returns per-block partial sums, and each lane
+//    applies its row's block scale with one FP32 FMA per partial.  Every
+//    product is exact; only the FP32 sums round.
+//  * The N activation columns of the current K chunk live in LDS, staged
+//    once per (matrix, chunk) by the whole workgroup, laid out so that each
+//    MFMA's A operand is one conflict-free 16-byte read per lane.
+//  * K is split into chunks only to fit LDS (<= 8704 k) or, for a single
+//    small GEMM, to give every wave work.  Partial sums of split tiles go
+//    to a workspace; the last wave to finish a tile (arrival counter) adds
+//    them in chunk order, so results never depend on timing.
+//  * A verify pass is one launch over a table of matrices: the units
+//    (matrix, chunk, 16-row tile) are split into one contiguous run per
+//    workgroup, balanced by bytes on the host.
+//
+// Numerics do not depend on N: a column's A rows, its MFMA sums, its FMA
+// rescale chain and its chunk sum are the same whatever the other columns
+// hold.  N only selects which LDS rows exist and which lanes read them.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wq_internal.h"
+
+namespace wq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+// Raw buffer resource word 3 for gfx9-family raw (untyped) buffer access.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy for the weight stream: non-temporal (read once).
+constexpr int kAuxStream = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAuxStream));
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kAuxStream));
+}
+__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kAuxStream);
+}
+
+// Eight E2M1 codes (one dword, low nibble first) -> eight exact BF16 values.
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t w) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+  return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// Eight E4M3 codes (two dwords, low byte first) -> eight exact BF16 values.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const char* lds, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(lds + off);
+}
+
+// ---- staging of one K chunk of X into LDS --------------------------------
+// LDS layout: piece (kc, n) = X[n][k0 + 8kc .. k0 + 8kc + 7] (16 bytes) at
+// byte (kc * N + n) * 16, for kc < kc_pad (pieces past the chunk are zero).
+template <int N>
+__device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0, int klen, int kc_pad) {
+  const int valid = klen / 8;
+  const int total = kc_pad * N;
+  for (int p0 = threadIdx.x; p0 < total; p0 += 4 * (int)blockDim.x) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = p0 + j * (int)blockDim.x;
+      const int n = p / kc_pad, kc = p - n * kc_pad;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (p < total && kc < valid)
+        v[j] = *reinterpret_cast<const u32x4*>(x + (size_t)n * K + k0 + 8 * kc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = p0 + j * (int)blockDim.x;
+      const int n = p / kc_pad, kc = p - n * kc_pad;
+      if (p < total) *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = v[j];
+    }
+  }
+}
+
+// ---- epilogue: lanes 0..31 hold sum[r] for n = 4*(lane/16) + r ----------
+template <int N>
+__device__ __forceinline__ void finish_tile(const DevMat& mt, int chunk, int tile, const float sum[4],
+                                            float mscale) {
+  const int lane = threadIdx.x & 63;
+  const int m = tile * 16 + (lane & 15);
+  const int nb = 4 * (lane >> 4);
+  const bool store_lane = lane < 32 && m < mt.M;
+  if (mt.nchunks == 1) {
+    if (store_lane) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (nb + r < N) mt.y[(size_t)(nb + r) * mt.M + m] = mscale * sum[r];
+    }
+    return;
+  }
+  // Split K: publish this chunk's partial, then let the last arrival add all
+  // chunks in chunk order.
+  if (store_lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (nb + r < N) mt.part[((size_t)chunk * N + nb + r) * mt.M + m] = sum[r];
+  }
+  __threadfence();
+  unsigned old = 0;
+  if (lane == 0) old = atomicAdd(mt.cnt + tile, 1u);
+  old = __shfl(old, 0);
+  if (old + 1 != (unsigned)mt.nchunks) return;
+  __threadfence();
+  if (store_lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (nb + r >= N) continue;
+      float t = 0.0f;
+      for (int c = 0; c < mt.nchunks; ++c)
+        t += __builtin_nontemporal_load(mt.part + ((size_t)c * N + nb + r) * mt.M + m);
+      mt.y[(size_t)(nb + r) * mt.M + m] = mscale * t;
+    }
+  }
+  if (lane == 0) atomicExch(mt.cnt + tile, 0u);
+}
+
+// ---- one NVFP4 unit: 16 rows x one K chunk --------------------------------
+template <int N, int PF, bool SALIGN>
+__device__ void nvfp4_unit(const DevMat& mt, int chunk, int tile, const char* lds) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int k0 = chunk * mt.kc;
+  const int klen = min(mt.kc, mt.K - k0);
+  const int nseg = (klen + 127) >> 7;
+  const uint64_t rowb = (uint64_t)mt.K >> 1, srowb = (uint64_t)mt.K >> 4;
+  const uint64_t m0 = (uint64_t)tile * 16;
+  const uint64_t cstart = m0 * rowb + (uint64_t)(k0 >> 1);
+  const uint64_t sstart = m0 * srowb + (uint64_t)(k0 >> 4);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(mt.w + cstart, (uint64_t)mt.M * rowb - cstart);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(mt.s + sstart, (uint64_t)mt.M * srowb - sstart);
+  const uint32_t voc = (uint32_t)(c * rowb) + 16u * g;
+  const uint32_t vos = (uint32_t)(c * srowb);
+
+  // A operand (X): lane (i = c, group g) is live when its row's block b = i/8
+  // matches the block of its k slots (g/2) and its column n = i%8 exists.
+  const bool active = ((c >> 3) == (g >> 1)) && ((c & 7) < N);
+  uint32_t xoff = active ? (uint32_t)((g * N + (c & 7)) * 16) : kZeroOffset<N>();
+  const uint32_t xstep = active ? 256u * N : 0u;
+
+  // scale bytes this lane applies: parity p of the 8 blocks of a segment
+  const uint32_t psel = (lane >> 5) ? 0x07050301u : 0x06040200u;
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  u32x4 cw[PF];
+  u32x2 sw[PF];
+  // Scale rows are 4-byte aligned when K % 64 == 0 (SALIGN); otherwise the
+  // eight scale bytes of a segment are fetched as four 2-byte loads and
+  // joined only when the segment is consumed.
+  uint32_t sh[SALIGN ? 1 : PF][4];
+  auto load = [&](int s, int slot) {
+    cw[slot] = bload16(rc, voc + 64u * s);
+    if constexpr (SALIGN) {
+      sw[slot] = bload8(rs, vos + 8u * s);
+    } else {
+      const uint32_t o = vos + 8u * s;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sh[slot][j] = bload2(rs, o + 2 * j);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (i < nseg) load(i, i);
+
+  for (int s0 = 0; s0 < nseg; s0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int s = s0 + i;
+      if (s >= nseg) break;
+      u32x4 d = cw[i];
+      u32x2 q;
+      if constexpr (SALIGN) {
+        q = sw[i];
+      } else {
+        q = u32x2{sh[i][0] | (sh[i][1] << 16), sh[i][2] | (sh[i][3] << 16)};
+      }
+      if (s + PF < nseg) load(s + PF, i);
+      // 4x4 dword transpose across the row's four lanes: afterwards lane
+      // group g holds, for MFMA step t, bytes [16t + 4g, 16t + 4g + 4) of the
+      // row's 64-byte segment, i.e. k = 32t + 8g .. 32t + 8g + 7.
+      u32x2 t0 = __builtin_amdgcn_permlane32_swap(d.x, d.z, false, false);
+      u32x2 t1 = __builtin_amdgcn_permlane32_swap(d.y, d.w, false, false);
+      u32x2 t2 = __builtin_amdgcn_permlane16_swap(t0.x, t1.x, false, false);
+      u32x2 t3 = __builtin_amdgcn_permlane16_swap(t0.y, t1.y, false, false);
+      const uint32_t e[4] = {t2.x, t2.y, t3.x, t3.y};
+      // block scales for steps t = 0..3 (blocks 2t + p of the segment)
+      uint32_t sb = __builtin_amdgcn_perm(q.y, q.x, psel);
+      const int vb = (klen - 128 * s) >> 4;  // scale blocks left in the chunk
+      if (vb < 8) sb &= (1u << (4 * vb)) - 1u;  // vb is even: keeps steps t < vb/2
+      const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
+      const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, true);
+      const float st[4] = {s01.x, s01.y, s23.x, s23.y};
+      const uint32_t xo = xoff + (uint32_t)s * xstep;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8 b = e2m1x8_to_bf16(e[t]);
+        const bf16x8 a = lds_read16(lds, xo + t * 64u * N);
+        const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(st[t], part[r], acc[r]);
+      }
+    }
+  }
+  // lanes l and l+32 hold blocks 0 and 1 of the same (n, m): add in that order
+  float sum[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u32x2 sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
+    sum[r] = acc[r] + __uint_as_float(sw2.y);
+  }
+  finish_tile<N>(mt, chunk, tile, sum, mt.g);
+}
+
+// ---- one FP8-row unit ------------------------------------------------------
+template <int N, int PF>
+__device__ void fp8_unit(const DevMat& mt, int chunk, int tile, const char* lds) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int k0 = chunk * mt.kc;
+  const int klen = min(mt.kc, mt.K - k0);
+  const int nseg = (klen + 63) >> 6;
+  const uint64_t rowb = (uint64_t)mt.K;
+  const uint64_t m0 = (uint64_t)tile * 16;
+  const uint64_t cstart = m0 * rowb + (uint64_t)k0;
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(mt.w + cstart, (uint64_t)mt.M * rowb - cstart);
+  const uint32_t voc = (uint32_t)(c * rowb) + 16u * g;
+
+  // A operand (X): rows i < N hold column i; k slots of group g at step u are
+  // k = 16g + 8u .. 16g + 8u + 7 of the segment.
+  const bool active = c < N;
+  uint32_t xoff = active ? (uint32_t)((2 * g * N + c) * 16) : kZeroOffset<N>();
+  const uint32_t xstep = active ? 128u * N : 0u;
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  u32x4 cw[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (i < nseg) cw[i] = bload16(rc, voc + 64u * i);
+
+  for (int s0 = 0; s0 < nseg; s0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int s = s0 + i;
+      if (s >= nseg) break;
+      u32x4 d = cw[i];
+      if (s + PF < nseg) cw[i] = bload16(rc, voc + 64u * (s + PF));
+      // In the chunk's last segment, lanes past its end may hold bytes of
+      // the next chunk or row; zero them (an E4M3 NaN times a zero X would
+      // still be NaN).
+      const int rem = klen - 64 * s;
+      if (rem < 64 && 16 * g >= rem) d = u32x4{0u, 0u, 0u, 0u};
+      const uint32_t xo = xoff + (uint32_t)s * xstep;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 b = e4m3x8_to_bf16(d[2 * u], d[2 * u + 1]);
+        const bf16x8 a = lds_read16(lds, xo + u * 16u * N);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+      }
+    }
+  }
+  const int m = tile * 16 + c;
+  const float rsc = (lane < 32 && m < mt.M) ? mt.rs[m] : 0.0f;
+  const float sum[4] = {acc[0], acc[1], acc[2], acc[3]};
+  finish_tile<N>(mt, chunk, tile, sum, rsc);
+}
+
+// ---- the persistent kernel -------------------------------------------------
+// Workgroup w processes units [range[w].begin, range[w+1].begin) of the
+// global unit list (matrix-major, then chunk, then tile).  For a single
+// matrix (mats == nullptr) the split is computed here, equal by units.
+template <int N, int MODE>
+__global__ __launch_bounds__(kThreads) void stream_kernel(const DevMat* __restrict__ mats,
+                                                          const WgRange* __restrict__ ranges,
+                                                          DevMat one) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  // wave-uniform values are pinned to scalar registers so that buffer
+  // resources built from them stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nwaves = kWaves;
+
+  int64_t u, u_end;
+  int mi;
+  if (mats == nullptr) {
+    const int64_t total = (int64_t)one.nchunks * one.ntiles;
+    u = total * blockIdx.x / gridDim.x;
+    u_end = total * (blockIdx.x + 1) / gridDim.x;
+    mi = 0;
+  } else {
+    u = ranges[blockIdx.x].begin;
+    u_end = ranges[blockIdx.x + 1].begin;
+    mi = ranges[blockIdx.x].mat;
+  }
+
+  // zero block read by lanes whose A-operand slots must be zero
+  for (int i = threadIdx.x; i < kZeroBytes<N>() / 16; i += blockDim.x)
+    *reinterpret_cast<u32x4*>(lds + kZeroOffset<N>() + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+
+  while (u < u_end) {
+    const DevMat mt = mats ? mats[mi] : one;
+    const int64_t mend = mt.unit0 + (int64_t)mt.nchunks * mt.ntiles;
+    if (u >= mend) { ++mi; continue; }
+    const int64_t local = u - mt.unit0;
+    const int chunk = (int)(local / mt.ntiles);
+    const int64_t run_end = min(u_end, mt.unit0 + (int64_t)(chunk + 1) * mt.ntiles);
+    const int k0 = chunk * mt.kc;
+    const int klen = min(mt.kc, mt.K - k0);
+    const int seg_k = mt.fmt == kFmtNvfp4 ? 128 : 64;
+    const int kc_pad = ((klen + seg_k - 1) / seg_k) * (seg_k / 8);
+    __syncthreads();
+    stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
+    __syncthreads();
+    for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
+      const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
+      if constexpr (MODE == kModeNvfp4Aligned) {
+        nvfp4_unit<N, kPrefetch, true>(mt, chunk, tile, lds);
+      } else if constexpr (MODE == kModeNvfp4) {
+        nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
+      } else if constexpr (MODE == kModeFp8) {
+        fp8_unit<N, kPrefetch>(mt, chunk, tile, lds);
+      } else {
+        if (mt.fmt == kFmtNvfp4)
+          nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
+        else
+          fp8_unit<N, kPrefetchGeneric>(mt, chunk, tile, lds);
+      }
+    }
+    u = run_end;
+  }
+}
+
+// ---- host-side launchers ---------------------------------------------------
+template <int N, int MODE>
+static hipError_t launch_nm(const DevMat* mats, const WgRange* ranges, const DevMat& one, int grid,
+                            size_t lds_bytes, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<N, MODE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((stream_kernel<N, MODE>), dim3(grid), dim3(kThreads), lds_bytes, stream, mats, ranges, one);
+  return hipGetLastError();
+}
+
+template <int N>
+static hipError_t launch_n(int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one, int grid,
+                           size_t lds_bytes, hipStream_t stream) {
+  switch (mode) {
+    case kModeNvfp4Aligned: return launch_nm<N, kModeNvfp4Aligned>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeNvfp4: return launch_nm<N, kModeNvfp4>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeFp8: return launch_nm<N, kModeFp8>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeMixed: return launch_nm<N, kModeMixed>(mats, ranges, one, grid, lds_bytes, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
+                         int grid, size_t lds_bytes, hipStream_t stream) {
+  switch (N) {
+    case 1: return launch_n<1>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    case 2: return launch_n<2>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    case 3: return launch_n<3>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    case 4: return launch_n<4>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    case 5: return launch_n<5>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    case 6: return launch_n<6>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    case 7: return launch_n<7>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    case 8: return launch_n<8>(mode, mats, ranges, one, grid, lds_bytes, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace wq

@@ -1,0 +1,195 @@
+"""ctypes binding of libwq.so: the same entry points as include/wq.h.
+
+This layer only marshals arguments: it takes torch tensors that already
+live on the GPU (or raw integer device pointers), passes their addresses,
+shapes and the current HIP stream to the C ABI, and raises on a non-zero
+status.  All arithmetic runs in the HIP kernels.  There is no fallback: if
+libwq.so has not been built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+
+WQ_FMT_NVFP4 = 0
+WQ_FMT_FP8ROW = 1
+
+STATUS_NAMES = {
+    0: "WQ_SUCCESS",
+    1: "WQ_ERROR_INVALID_VALUE",
+    2: "WQ_ERROR_UNSUPPORTED_SHAPE",
+    3: "WQ_ERROR_MISALIGNED",
+    4: "WQ_ERROR_WORKSPACE",
+    5: "WQ_ERROR_LAUNCH",
+    6: "WQ_ERROR_DEVICE",
+}
+
+
+class WQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (where, STATUS_NAMES.get(status, "unknown"), status))
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libwq.so is not built; run `python -m fp8_weight_streaming_amd.build` "
+                      "(hipcc for gfx950) -- there is no CPU fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class WqMatrix(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("M", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("global_scale", ctypes.c_float), ("w", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_S = ctypes.c_size_t
+_lib.wq_status_string.restype = ctypes.c_char_p
+_lib.wq_status_string.argtypes = [_I]
+_lib.wq_gemm_workspace_bytes.restype = _S
+_lib.wq_gemm_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.wq_gemm_split.restype = _I
+_lib.wq_gemm_split.argtypes = [_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.wq_gemm_nvfp4.restype = _I
+_lib.wq_gemm_nvfp4.argtypes = [_P, _P, ctypes.c_float, _P, _P, _I, _I, _I, _P, _S, _P]
+_lib.wq_gemm_fp8row.restype = _I
+_lib.wq_gemm_fp8row.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _S, _P]
+_lib.wq_verify_workspace_bytes.restype = _S
+_lib.wq_verify_workspace_bytes.argtypes = [ctypes.POINTER(WqMatrix), _I, _I]
+_lib.wq_verify_pass.restype = _I
+_lib.wq_verify_pass.argtypes = [ctypes.POINTER(WqMatrix), _I, _I, _P, _S, _P]
+
+EXPORTED = ["wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4",
+            "wq_gemm_fp8row", "wq_verify_workspace_bytes", "wq_verify_pass"]
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("libwq takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libwq takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise WQError(status, where)
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None or isinstance(t, int) else t.numel() * t.element_size()
+
+
+def wq_status_string(status: int) -> str:
+    return _lib.wq_status_string(status).decode()
+
+
+def wq_gemm_workspace_bytes(fmt: int, M: int, K: int, N: int) -> int:
+    return int(_lib.wq_gemm_workspace_bytes(fmt, M, K, N))
+
+
+def wq_gemm_split(fmt: int, M: int, K: int, in_verify_pass: bool = False):
+    """(k_chunk, n_chunks) the call would use."""
+    kc, nc = _I(0), _I(0)
+    _check(_lib.wq_gemm_split(fmt, M, K, 1 if in_verify_pass else 0, ctypes.byref(kc), ctypes.byref(nc)),
+           "wq_gemm_split")
+    return kc.value, nc.value
+
+
+def wq_gemm_nvfp4(codes, scales, global_scale: float, x, y, workspace=None, stream=None,
+                  M: Optional[int] = None, K: Optional[int] = None, N: Optional[int] = None,
+                  workspace_bytes: Optional[int] = None):
+    """y[N, M] = x[N, K] . W^T for NVFP4 W (codes uint8 [M, K/2], scales uint8 [M, K/16]).
+
+    Tensors are torch device tensors (x as int16/uint16/bfloat16 bits, y float32);
+    shapes are taken from them unless given explicitly (raw-pointer use)."""
+    if M is None:
+        M = codes.shape[0]
+    if K is None:
+        K = 2 * codes.shape[1]
+    if N is None:
+        N = x.shape[0]
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_gemm_nvfp4(_ptr(codes), _ptr(scales), float(global_scale), _ptr(x), _ptr(y), M, K, N,
+                              _ptr(workspace), wsb, _stream(stream)), "wq_gemm_nvfp4")
+
+
+def wq_gemm_fp8row(w, row_scale, x, y, workspace=None, stream=None, M: Optional[int] = None,
+                   K: Optional[int] = None, N: Optional[int] = None, workspace_bytes: Optional[int] = None):
+    """y[N, M] = x[N, K] . W^T for row-scaled FP8 W (w uint8 [M, K], row_scale float32 [M])."""
+    if M is None:
+        M = w.shape[0]
+    if K is None:
+        K = w.shape[1]
+    if N is None:
+        N = x.shape[0]
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_gemm_fp8row(_ptr(w), _ptr(row_scale), _ptr(x), _ptr(y), M, K, N, _ptr(workspace), wsb,
+                               _stream(stream)), "wq_gemm_fp8row")
+
+
+@dataclass
+class Matrix:
+    """One matrix of a verify pass (device tensors or raw pointers)."""
+    fmt: int
+    M: int
+    K: int
+    w: object
+    scales: object
+    x: object
+    y: object
+    global_scale: float = 1.0
+
+
+def _descs(mats: Sequence[Matrix]):
+    arr = (WqMatrix * len(mats))()
+    for i, m in enumerate(mats):
+        arr[i] = WqMatrix(m.fmt, m.M, m.K, float(m.global_scale), _ptr(m.w), _ptr(m.scales), _ptr(m.x),
+                          _ptr(m.y))
+    return arr
+
+
+def wq_verify_workspace_bytes(mats: Sequence[Matrix], N: int) -> int:
+    arr = _descs(mats)
+    return int(_lib.wq_verify_workspace_bytes(arr, len(mats), N))
+
+
+def wq_verify_pass(mats: Sequence[Matrix], N: int, workspace, stream=None, workspace_bytes: Optional[int] = None):
+    """All matrices at N columns in one persistent launch."""
+    arr = _descs(mats)
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_verify_pass(arr, len(mats), N, _ptr(workspace), wsb, _stream(stream)), "wq_verify_pass")
+
+
+def descriptor_array(mats: Sequence[Matrix]):
+    """The ctypes descriptor array (for callers that reuse it across calls)."""
+    return _descs(mats)
+
+
+def verify_pass_raw(arr, count: int, N: int, workspace_ptr: int, workspace_bytes: int, stream: int):
+    _check(_lib.wq_verify_pass(arr, count, N, workspace_ptr, workspace_bytes, stream), "wq_verify_pass")

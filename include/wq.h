@@ -1,0 +1,149 @@
+/*
+ * wq.h -- C ABI of libwq: the weight-streaming skinny GEMM of a
+ * speculative-decoding verify pass, on AMD MI355X (gfx950).
+ *
+ * Operation (every entry point):
+ *     Y[n][m] = sum_k W[m][k] * X[n][k],   0 <= n < N <= 8, 0 <= m < M
+ * with X in BF16, Y in FP32 (FP32 accumulation) and W in one of two stored
+ * formats.  This is the product the crit-hub engine card
+ * "mtp7-device-confidence" runs for its verify pass (section "Design", rows
+ * "Decode" and "GEMVs": one target pass over the drafted columns, 2-8 of
+ * them, reading FP8 and NVFP4 weight bytes directly; N = 1 is plain
+ * decode), and which its section "Measured" prices by the bytes it reads.
+ *
+ * Conventions shared by all calls
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees, copies to the host or synchronizes;
+ *    a call only enqueues work on `stream` (a hipStream_t; NULL means the
+ *    default stream).  The caller keeps every buffer alive until that
+ *    work has completed.
+ *  - Inputs are read-only.  Y must not alias any input.  Y is overwritten
+ *    (never accumulated into).
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    any error the call returns a status other than WQ_SUCCESS and has
+ *    launched nothing.  Faults during execution surface at the caller's
+ *    next synchronization of `stream`.
+ *  - Results are deterministic: the same inputs give the same bits on
+ *    every call, and column n of Y does not depend on N or on the other
+ *    columns of X (the crit-hub card's section "Checks" asks for GEMVs at
+ *    1-8 columns "with column invariance"; the crit README's "Kernel
+ *    workbench" asks for the same bits on a repeat).  How K is split
+ *    depends only on (M, K) and the device, never on N.
+ *  - Workspace: some shapes split K across workgroups and need scratch
+ *    memory (partial sums and per-tile arrival counters).  Query its size
+ *    with the matching *_workspace_bytes call; pass a device buffer at
+ *    least that large (16-byte aligned), or NULL/0 when the query returns
+ *    0.  The buffer must be zero-filled before its first use with this
+ *    library; every completed call leaves its counters at zero again, so
+ *    a workspace can be reused by later calls of any shape.  Calls that
+ *    share one workspace must not overlap in time (same stream is fine).
+ *  - Threading: the library keeps no state besides a per-device cache of
+ *    the compute-unit count; calls are reentrant on different streams with
+ *    different workspaces.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum wq_status {
+  WQ_SUCCESS = 0,
+  WQ_ERROR_INVALID_VALUE = 1,     /* NULL pointer, N outside 1..8, M or K < 1, count < 1, bad format */
+  WQ_ERROR_UNSUPPORTED_SHAPE = 2, /* K not a multiple of 32 (NVFP4) or 16 (FP8-row), or too large */
+  WQ_ERROR_MISALIGNED = 3,        /* an array pointer not 16-byte aligned */
+  WQ_ERROR_WORKSPACE = 4,         /* workspace NULL or smaller than the query returned */
+  WQ_ERROR_LAUNCH = 5,            /* the HIP runtime refused a launch or a copy */
+  WQ_ERROR_DEVICE = 6             /* no current HIP device, or not a gfx950 device */
+} wq_status;
+
+enum { WQ_FMT_NVFP4 = 0, WQ_FMT_FP8ROW = 1 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* wq_status_string(wq_status s);
+
+/* Bytes of workspace wq_gemm_nvfp4 (fmt = WQ_FMT_NVFP4) or wq_gemm_fp8row
+ * (fmt = WQ_FMT_FP8ROW) needs for this shape on the current device; 0 when
+ * the shape is computed without splitting K.  Returns 0 for invalid
+ * arguments too (the GEMM call then reports the error). */
+size_t wq_gemm_workspace_bytes(int fmt, int M, int K, int N);
+
+/* The K split a call will use: K is cut into *n_chunks chunks of *k_chunk
+ * (the last may be shorter).  in_verify_pass = 0 asks about
+ * wq_gemm_nvfp4 / wq_gemm_fp8row on the current device, 1 about a matrix
+ * inside wq_verify_pass.  Two calls that report the same split compute
+ * bit-identical results for the same matrix and columns. */
+wq_status wq_gemm_split(int fmt, int M, int K, int in_verify_pass, int* k_chunk, int* n_chunks);
+
+/* NVFP4 weights.
+ *   codes  [M][K/2] uint8: two E2M1 codes per byte; byte j of row m holds
+ *          k = 2j in its low nibble and k = 2j+1 in its high nibble.
+ *          E2M1: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0.
+ *   scales [M][K/16] uint8: one E4M3 (FN) scale per 16 consecutive k;
+ *          scale b of row m covers k in [16b, 16b+16).  NaN scales
+ *          propagate to the outputs they touch.
+ *   global_scale  FP32 per-tensor multiplier (not its reciprocal).
+ *   x      [N][K] BF16 bit patterns, row-major (row n = column n of X).
+ *   y      [N][M] FP32, row-major, overwritten.
+ *   W[m][k] = e2m1(code) * e4m3(scale) * global_scale.
+ * Requirements: 1 <= N <= 8, M >= 1, K >= 32, K % 32 == 0, M*K/2 < 2^40,
+ * codes/scales/x/y 16-byte aligned (x's row stride K*2 bytes is then a
+ * multiple of 64; scales' row stride K/16 bytes need only be a multiple
+ * of 2, which K % 32 == 0 gives). */
+wq_status wq_gemm_nvfp4(const uint8_t* codes, const uint8_t* scales, float global_scale,
+                        const uint16_t* x, float* y, int M, int K, int N,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Row-scaled FP8-E4M3 weights (the card's section "Model": projections and
+ * output head stored or re-encoded as FP8 with one scale per output row).
+ *   w         [M][K] uint8 E4M3 (FN) codes.
+ *   row_scale [M] FP32; W[m][k] = e4m3(w[m][k]) * row_scale[m].
+ *   x, y      as for wq_gemm_nvfp4.
+ * Requirements: 1 <= N <= 8, M >= 1, K >= 16, K % 16 == 0, M*K < 2^40,
+ * w/row_scale/x/y 16-byte aligned. */
+wq_status wq_gemm_fp8row(const uint8_t* w, const float* row_scale,
+                         const uint16_t* x, float* y, int M, int K, int N,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* One matrix of a verify pass (host-side descriptor).  For WQ_FMT_NVFP4,
+ * `w` = codes, `scales` = block scales, `global_scale` used; for
+ * WQ_FMT_FP8ROW, `w` = E4M3 codes, `scales` = the FP32 row scales
+ * (reinterpreted), `global_scale` ignored.  x [N][K], y [N][M] as above. */
+typedef struct wq_matrix {
+  int32_t fmt;
+  int32_t M;
+  int32_t K;
+  float global_scale;
+  const void* w;
+  const void* scales;
+  const uint16_t* x;
+  float* y;
+} wq_matrix;
+
+/* Workspace bytes wq_verify_pass needs for these descriptors (the
+ * device-side copy of the descriptor table plus split-K scratch). */
+size_t wq_verify_workspace_bytes(const wq_matrix* descs, int count, int N);
+
+/* A whole verify pass: `count` independent products, all at the same N,
+ * in ONE persistent kernel launch, so that small matrices do not leave
+ * HBM idle between launches (the card's section "Decode": the verify pass
+ * for the drafts made runs as one node of the round's graph).  `descs` is
+ * a HOST array; it is validated, then copied into `workspace` with an
+ * asynchronous host-to-device copy on `stream` (so the call is not
+ * capture-safe unless the host array is pinned).  Each matrix obeys the
+ * requirements of its format's GEMM call; matrices may differ in format
+ * and shape.  Results equal, bit for bit, those of the single-matrix
+ * calls whenever wq_gemm_split reports the same split for both; otherwise
+ * they agree to FP32 rounding of the sums. */
+wq_status wq_verify_pass(const wq_matrix* descs, int count, int N,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,108 @@
+"""The C ABI library on the host: it loads, exports every function that
+include/wq.h declares, and rejects bad arguments before touching the GPU.
+
+Nothing here launches a kernel; the validation paths return their status
+without any HIP call, so these tests run on a machine with no GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(wq_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def wq():
+    from fp8_weight_streaming_amd import wq as mod
+    return mod
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["wq_gemm_nvfp4", "wq_gemm_fp8row", "wq_verify_pass", "wq_gemm_workspace_bytes",
+              "wq_verify_workspace_bytes", "wq_status_string", "wq_gemm_split"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(wq):
+    lib = ctypes.CDLL(wq.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(wq.EXPORTED) == declared_functions()
+
+
+def test_status_strings(wq):
+    assert wq.wq_status_string(0) == "success"
+    for s in range(1, 7):
+        assert wq.wq_status_string(s) not in ("", "unknown status")
+    assert wq.wq_status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20          # 16-byte aligned fake device address; never dereferenced
+MISALIGNED = FAKE + 4
+
+
+def nv(lib, codes=FAKE, scales=FAKE, x=FAKE, y=FAKE, M=64, K=128, N=4, ws=0, wsb=0):
+    return lib.wq_gemm_nvfp4(codes, scales, 1.0, x, y, M, K, N, ws, wsb, 0)
+
+
+def fp8(lib, w=FAKE, rs=FAKE, x=FAKE, y=FAKE, M=64, K=128, N=4, ws=0, wsb=0):
+    return lib.wq_gemm_fp8row(w, rs, x, y, M, K, N, ws, wsb, 0)
+
+
+def test_gemm_argument_errors(wq):
+    lib = wq.lib()
+    INV, SHAPE, MIS = 1, 2, 3
+    assert nv(lib, codes=0) == INV
+    assert nv(lib, scales=0) == INV
+    assert nv(lib, x=0) == INV
+    assert nv(lib, y=0) == INV
+    assert nv(lib, N=0) == INV and nv(lib, N=9) == INV and nv(lib, N=-1) == INV
+    assert nv(lib, M=0) == INV and nv(lib, K=0) == INV
+    assert nv(lib, K=48) == SHAPE and nv(lib, K=16) == SHAPE and nv(lib, K=(1 << 24) + 32) == SHAPE
+    assert nv(lib, M=1 << 30, K=1 << 12) == SHAPE
+    assert nv(lib, codes=MISALIGNED) == MIS and nv(lib, y=MISALIGNED) == MIS and nv(lib, x=FAKE + 8) == MIS
+    assert fp8(lib, w=0) == INV and fp8(lib, rs=0) == INV
+    assert fp8(lib, K=40) == SHAPE and fp8(lib, K=8) == SHAPE
+    assert fp8(lib, rs=MISALIGNED) == MIS
+    assert fp8(lib, N=9) == INV
+
+
+def test_verify_argument_errors(wq):
+    lib = wq.lib()
+    good = wq.WqMatrix(0, 64, 128, 1.0, FAKE, FAKE, FAKE, FAKE)
+    arr = (wq.WqMatrix * 2)(good, good)
+    assert lib.wq_verify_pass(arr, 0, 4, FAKE, 1 << 20, 0) == 1
+    assert lib.wq_verify_pass(None, 2, 4, FAKE, 1 << 20, 0) == 1
+    assert lib.wq_verify_pass(arr, 2, 0, FAKE, 1 << 20, 0) == 1
+    assert lib.wq_verify_pass(arr, 2, 4, 0, 1 << 20, 0) == 4
+    assert lib.wq_verify_pass(arr, 2, 4, MISALIGNED, 1 << 20, 0) == 3
+    arr[1] = wq.WqMatrix(0, 64, 96 + 8, 1.0, FAKE, FAKE, FAKE, FAKE)
+    assert lib.wq_verify_pass(arr, 2, 4, FAKE, 1 << 20, 0) == 2
+    arr[1] = wq.WqMatrix(1, 64, 96, 1.0, FAKE, 0, FAKE, FAKE)
+    assert lib.wq_verify_pass(arr, 2, 4, FAKE, 1 << 20, 0) == 1
+    arr[1] = wq.WqMatrix(7, 64, 96, 1.0, FAKE, FAKE, FAKE, FAKE)
+    assert lib.wq_verify_pass(arr, 2, 4, FAKE, 1 << 20, 0) == 1
+    assert lib.wq_verify_workspace_bytes(arr, 2, 4) == 0  # invalid descriptor -> 0
+
+
+def test_split_query_rejects_bad_args(wq):
+    lib = wq.lib()
+    kc, nc = ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.wq_gemm_split(0, 64, 48, 1, ctypes.byref(kc), ctypes.byref(nc)) == 2
+    assert lib.wq_gemm_split(0, 64, 128, 1, None, ctypes.byref(nc)) == 1
+    # inside a verify pass the split depends only on (M, K): no device needed
+    assert lib.wq_gemm_split(0, 5120, 17408, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (8704, 2)
+    assert lib.wq_gemm_split(0, 7168, 5120, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (5120, 1)
+    assert lib.wq_gemm_split(1, 151936, 5120, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (5120, 1)
