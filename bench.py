@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark: one dense verify pass per step on one MI355X.
+
+Workload (the dense verify-pass configuration): 64 layers x {qkv 7168x5120,
+o 5120x6144, gate+up 34816x5120, down 5120x17408}, every matrix NVFP4
+(21,474,836,480 weights, 12,079,595,520 weight bytes), BF16 activations,
+N cycled over 2, 4, 8 from one pass to the next, all 256 matrices in one
+persistent launch (wq_verify_launch of a prepared plan).  Inputs are
+seeded synthetic arrays (fp8_weight_streaming_amd.inputs), resident in HBM
+before the timed region.
+
+Printed: ONE JSON line with the metric (achieved HBM GB/s over the timed
+passes, algorithmic bytes per pass / pass time), the per-N breakdown, a
+roofline object for the verify kernel (HIP events on the launch stream),
+the CPU oracle's rate on a bounded sample, and a parity check of sampled
+output rows against the oracle.
+
+    python bench.py [--gpus 1] [--steps 90] [--warmup 9]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import mmap
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from fp8_weight_streaming_amd import inputs  # noqa: E402
+
+METRIC = "achieved HBM GB/s (% of peak) and µs per verify pass, N=1..8 columns"
+PEAK_GBPS = 8000.0
+N_CYCLE = [2, 4, 8]
+NMAX = 8
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_pass_traffic.txt")
+KERNEL_SOURCES = ["fp8_weight_streaming_amd/csrc/wq_kernels.hip", "fp8_weight_streaming_amd/csrc/wq_internal.h"]
+
+
+# ---- input generation (before the GPU is touched) ---------------------------
+
+_SHARED = {}
+
+
+def _layout(wl):
+    offs, tot = [], [0, 0, 0]
+    for spec in wl.matrices:
+        sizes = (spec.M * spec.K // 2, spec.M * spec.K // 16, NMAX * spec.K * 2)
+        offs.append(tuple(tot))
+        for j in range(3):
+            tot[j] += sizes[j]
+    return offs, tot
+
+
+def _gen_worker(i):
+    import torch
+    torch.set_num_threads(1)
+    wl, offs = _SHARED["wl"], _SHARED["offs"]
+    spec = wl.matrices[i]
+    d = inputs.nvfp4_inputs(spec.M, spec.K, NMAX, wl.seed(i), wl.g, wl.x_scale)
+    oc, os_, ox = offs[i]
+    np.frombuffer(_SHARED["codes"], np.uint8, d.codes.size, oc)[:] = d.codes.reshape(-1)
+    np.frombuffer(_SHARED["scales"], np.uint8, d.scales.size, os_)[:] = d.scales.reshape(-1)
+    np.frombuffer(_SHARED["x"], np.uint8, d.x.size * 2, ox)[:] = d.x.reshape(-1).view(np.uint8)
+    return i
+
+
+def generate(wl, workers):
+    """Draw every matrix of the pass into shared anonymous memory, with a
+    pool of forked workers (workers = 0: in this process, e.g. under a
+    profiler that has already initialised the GPU)."""
+    offs, tot = _layout(wl)
+    _SHARED.update(wl=wl, offs=offs, codes=mmap.mmap(-1, tot[0]), scales=mmap.mmap(-1, tot[1]),
+                   x=mmap.mmap(-1, tot[2]))
+    if workers <= 0:
+        for i in range(len(wl.matrices)):
+            _gen_worker(i)
+    else:
+        ctx = mp.get_context("fork")
+        with ctx.Pool(workers) as pool:
+            for _ in pool.imap_unordered(_gen_worker, range(len(wl.matrices)), chunksize=1):
+                pass
+    host = []
+    for i, spec in enumerate(wl.matrices):
+        oc, os_, ox = offs[i]
+        codes = np.frombuffer(_SHARED["codes"], np.uint8, spec.M * spec.K // 2, oc).reshape(spec.M, spec.K // 2)
+        scales = np.frombuffer(_SHARED["scales"], np.uint8, spec.M * spec.K // 16, os_).reshape(spec.M, spec.K // 16)
+        x = np.frombuffer(_SHARED["x"], np.uint16, NMAX * spec.K, ox).reshape(NMAX, spec.K)
+        host.append(inputs.NVFP4Inputs(codes=codes, scales=scales, g=wl.g, x=x))
+    return host
+
+
+# ---- byte accounting -----------------------------------------------------------
+
+def algorithmic_bytes(wl, N):
+    """Bytes the method must move for one pass at N columns: 0.5625 B per
+    NVFP4 weight (codes + block scales), the BF16 activations (2NK per
+    matrix), the FP32 outputs (4NM) and the 4-byte tensor scale."""
+    tot = 0
+    for s in wl.matrices:
+        tot += s.M * s.K // 2 + s.M * s.K // 16 + 2 * N * s.K + 4 * N * s.M + 4
+    return tot
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None, None
+    kv = {}
+    with open(PROFILE_TRAFFIC) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, kv
+    try:
+        return float(kv["hbm_bytes_per_launch_mean"]), kv
+    except (KeyError, ValueError):
+        return None, kv
+
+
+# ---- CPU baseline ----------------------------------------------------------------
+
+def cpu_baseline(wl, host, budget_s=12.0, max_layers=8):
+    """The oracle, as it is, on the first layers of the same pass: every
+    matrix of layer l at N = 2, 4 and 8, layer after layer until `budget_s`
+    seconds of CPU time have been spent (at most `max_layers` layers)."""
+    import oracle
+    t0 = time.perf_counter()
+    nbytes, layers = 0, 0
+    while layers < max_layers:
+        for j in range(4):
+            i = 4 * layers + j
+            d = host[i]
+            for N in N_CYCLE:
+                oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N])
+                s = wl.matrices[i]
+                nbytes += s.M * s.K // 2 + s.M * s.K // 16 + 2 * N * s.K + 4 * N * s.M + 4
+        layers += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "FP64 oracle (C, OpenMP) on all rows of layers 0..%d (%d matrices) at N=2,4,8: %.3f GB "
+                      "algorithmic in %.1f s" % (layers - 1, 4 * layers, nbytes / 1e9, dt)}
+
+
+# ---- main ------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=90)
+    ap.add_argument("--warmup", type=int, default=9)
+    ap.add_argument("--layers", type=int, default=64, help="layers of the pass (64 is the measured workload)")
+    ap.add_argument("--check-rows", type=int, default=32, help="sampled rows per matrix checked against the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path (the matrices of a verify pass are "
+              "independent and would shard by rows or by matrix with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    wl = inputs.workload(3, layers=args.layers)
+    t_gen = time.perf_counter()
+    print("[bench] generating %d matrices with %d workers" % (len(wl.matrices), args.workers), file=sys.stderr,
+          flush=True)
+    host = generate(wl, args.workers)
+    t_gen = time.perf_counter() - t_gen
+    print("[bench] generated in %.1f s" % t_gen, file=sys.stderr, flush=True)
+
+    import torch
+    from fp8_weight_streaming_amd import wq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # upload: inputs resident in HBM before anything is timed
+    mats_dev = []
+    for i, (spec, d) in enumerate(zip(wl.matrices, host)):
+        codes = torch.from_numpy(d.codes).to(dev)
+        scales = torch.from_numpy(d.scales).to(dev)
+        x = torch.from_numpy(d.x.view(np.int16)).to(dev)
+        y = torch.zeros((NMAX, spec.M), dtype=torch.float32, device=dev)
+        mats_dev.append((codes, scales, x, y))
+    torch.cuda.synchronize()
+    print("[bench] uploaded %.2f GB" % (sum(c.numel() + s.numel() for c, s, _, _ in mats_dev) / 1e9),
+          file=sys.stderr, flush=True)
+
+    plans, keep = {}, []
+    for N in N_CYCLE:
+        mats = [wq.Matrix(wq.WQ_FMT_NVFP4, s.M, s.K, c, sc, x[:N], y[:N], wl.g)
+                for s, (c, sc, x, y) in zip(wl.matrices, mats_dev)]
+        nbytes = wq.wq_verify_workspace_bytes(mats, N)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        plans[N] = wq.wq_verify_prepare(mats, N, ws, stream)
+        keep.append((mats, ws))
+    torch.cuda.synchronize()
+
+    # attainable read rate (probe) and a copy of known size (counter scale)
+    probe_buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    probe_buf.fill_(1)
+    sink = torch.empty(wq.wq_probe_sink_words(), dtype=torch.int32, device=dev)
+    for _ in range(2):
+        wq.wq_probe_read(probe_buf, sink, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        wq.wq_probe_read(probe_buf, sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    probe_gbps = 5 * probe_buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    copy_dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    wq.wq_probe_copy(probe_buf[: 1 << 30], copy_dst, stream)
+    torch.cuda.synchronize()
+    del probe_buf, copy_dst
+
+    # warmup
+    for i in range(args.warmup):
+        wq.wq_verify_launch(plans[N_CYCLE[i % 3]], stream)
+    torch.cuda.synchronize()
+
+    # timed region
+    steps = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ns = [N_CYCLE[i % 3] for i in range(steps)]
+    launch = wq.lib().wq_verify_launch
+    import ctypes
+    plan_refs = {N: ctypes.byref(plans[N]) for N in N_CYCLE}
+    sptr = stream.cuda_stream
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        st = launch(plan_refs[ns[i]], sptr)
+        ev[i][1].record(stream)
+        if st != 0:
+            raise RuntimeError("wq_verify_launch failed: %d" % st)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    wall_s = t1 - t0
+    durs = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])  # seconds per launch
+    bytes_n = {N: algorithmic_bytes(wl, N) for N in N_CYCLE}
+    total_bytes = sum(bytes_n[N] for N in ns)
+    value = total_bytes / wall_s / 1e9
+    per_n = {}
+    for N in N_CYCLE:
+        d = durs[[j for j in range(steps) if ns[j] == N]]
+        per_n[str(N)] = {"us_per_pass_mean": float(d.mean() * 1e6), "us_per_pass_min": float(d.min() * 1e6),
+                         "algorithmic_bytes": bytes_n[N],
+                         "gbps": float(bytes_n[N] / d.mean() / 1e9),
+                         "pct_of_8TBps": float(100 * bytes_n[N] / d.mean() / 1e9 / PEAK_GBPS)}
+    kernel_s = float(durs.sum())
+    achieved = total_bytes / kernel_s / 1e9
+    traffic, traffic_kv = read_traffic()
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_GBPS, "traffic": traffic,
+                "kernel": "wq::stream_kernel<N, mode 0> (one launch per verify pass)",
+                "avg_launch_us": kernel_s / steps * 1e6,
+                "algorithmic_bytes_per_launch_mean": total_bytes / steps,
+                "probe_read_gbps": probe_gbps, "frac_of_probe": achieved / probe_gbps}
+
+    # parity: sampled rows of every matrix at every N against the oracle
+    import oracle
+    rng = np.random.default_rng(12345)
+    worst, rows_checked, ok = 0.0, 0, True
+    for N in N_CYCLE:
+        wq.wq_verify_launch(plans[N], stream)
+        torch.cuda.synchronize()
+        for i, (spec, d) in enumerate(zip(wl.matrices, host)):
+            rows = np.unique(np.concatenate([rng.integers(0, spec.M, args.check_rows), [0, spec.M - 1]]))
+            y = mats_dev[i][3][:N].cpu().numpy()[:, rows].astype(np.float64)
+            yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N], rows=rows)
+            err = np.abs(y - yr)
+            bound = 1e-3 * ar
+            bad = err > bound
+            if bad.any() or np.isnan(y).any():
+                ok = False
+            worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
+            rows_checked += rows.size * N
+    parity = {"ok": ok, "elements_checked": rows_checked, "max_err_over_bound": worst,
+              "bound": "|y - y_oracle| <= 1e-3 * sum|w*x|"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, host)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_s / steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": args.layers, "matrices": len(wl.matrices),
+                   "weight_format": "nvfp4 (e2m1 codes, e4m3 scale per 16 k, fp32 tensor scale)",
+                   "activations": "bf16", "outputs": "fp32", "n_cycle": N_CYCLE,
+                   "weight_bytes_per_pass": sum(s.M * s.K // 2 + s.M * s.K // 16 for s in wl.matrices),
+                   "pct_of_8TBps": 100 * value / PEAK_GBPS,
+                   "us_per_pass": wall_s / steps * 1e6},
+        "per_n": per_n,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(out))
+    if not ok:
+        print("[bench] PARITY FAILED", file=sys.stderr)
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -124,11 +124,10 @@ wq_status check_ptrs(const void* w, const void* s, const void* x, const void* y)
   return WQ_SUCCESS;
 }
 
-// Workspace bytes of the split-K scratch of one matrix.
+// Workspace bytes of the split-K scratch (chunk partial sums) of one matrix.
 size_t split_scratch_bytes(const Split& s, int M, int N) {
   if (s.nchunks <= 1) return 0;
-  return align_up((size_t)s.nchunks * N * M * sizeof(float), kAlign) +
-         align_up((size_t)s.ntiles * sizeof(unsigned), kAlign);
+  return align_up((size_t)s.nchunks * N * M * sizeof(float), kAlign);
 }
 
 DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x, float* y, int M, int K,
@@ -147,10 +146,7 @@ DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x
   d.nchunks = sp.nchunks;
   d.ntiles = sp.ntiles;
   d.unit0 = unit0;
-  if (sp.nchunks > 1) {
-    d.part = reinterpret_cast<float*>(scratch);
-    d.cnt = reinterpret_cast<unsigned*>(scratch + align_up((size_t)sp.nchunks * N * M * sizeof(float), kAlign));
-  }
+  if (sp.nchunks > 1) d.part = reinterpret_cast<float*>(scratch);
   return d;
 }
 
@@ -170,8 +166,11 @@ wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x
   const int64_t units = (int64_t)sp.nchunks * sp.ntiles;
   const int grid = (int)std::min<int64_t>(cus, units);
   const int mode = fmt == kFmtFp8Row ? kModeFp8 : (K % 64 == 0 ? kModeNvfp4Aligned : kModeNvfp4);
-  const hipError_t e = launch_stream(N, mode, nullptr, nullptr, one, grid, lds_bytes_for(N),
-                                     static_cast<hipStream_t>(stream));
+  hipError_t e = launch_stream(N, mode, nullptr, nullptr, one, grid, lds_bytes_for(N),
+                               static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && sp.nchunks > 1)
+    e = launch_reduce(nullptr, nullptr, one, (int)ceil_div((int64_t)N * M, kReduceRun), N,
+                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
 }
 
@@ -179,7 +178,8 @@ wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x
 struct PassLayout {
   std::vector<Split> splits;
   std::vector<size_t> scratch_off;
-  size_t table_bytes = 0, ranges_bytes = 0, scratch_bytes = 0, total = 0;
+  std::vector<ReduceTask> tasks;  // reduction runs of the split matrices
+  size_t table_bytes = 0, ranges_bytes = 0, tasks_bytes = 0, scratch_bytes = 0, total = 0;
   int grid = 0;
   int64_t units = 0;
 };
@@ -205,15 +205,22 @@ PassLayout pass_layout(const wq_matrix* descs, int count, int N, int cus) {
     L.units += (int64_t)L.splits[i].nchunks * L.splits[i].ntiles;
   }
   L.grid = (int)std::min<int64_t>(cus, L.units);
+  for (int i = 0; i < count; ++i) {
+    if (L.splits[i].nchunks <= 1) continue;
+    const int64_t outs = (int64_t)N * descs[i].M;
+    for (int64_t b = 0; b < outs; b += kReduceRun)
+      L.tasks.push_back(ReduceTask{b, i, (int32_t)std::min<int64_t>(kReduceRun, outs - b)});
+  }
   L.table_bytes = align_up((size_t)count * sizeof(DevMat), kAlign);
   L.ranges_bytes = align_up((size_t)(L.grid + 1) * sizeof(WgRange), kAlign);
+  L.tasks_bytes = align_up(L.tasks.size() * sizeof(ReduceTask), kAlign);
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     L.scratch_off[i] = off;
     off += split_scratch_bytes(L.splits[i], descs[i].M, N);
   }
   L.scratch_bytes = off;
-  L.total = L.table_bytes + L.ranges_bytes + L.scratch_bytes;
+  L.total = L.table_bytes + L.ranges_bytes + L.tasks_bytes + L.scratch_bytes;
   return L;
 }
 
@@ -317,8 +324,9 @@ size_t wq_verify_workspace_bytes(const wq_matrix* descs, int count, int N) {
   return pass_layout(descs, count, N, cus).total;
 }
 
-wq_status wq_verify_pass(const wq_matrix* descs, int count, int N, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* workspace, size_t workspace_bytes,
+                            void* stream, wq_verify_plan* plan) {
+  if (!plan) return WQ_ERROR_INVALID_VALUE;
   wq_status st = check_descs(descs, count, N);
   if (st != WQ_SUCCESS) return st;
   if (!workspace) return WQ_ERROR_WORKSPACE;
@@ -328,41 +336,70 @@ wq_status wq_verify_pass(const wq_matrix* descs, int count, int N, void* workspa
   const PassLayout L = pass_layout(descs, count, N, cus);
   if (workspace_bytes < L.total) return WQ_ERROR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
-  char* scratch = ws + L.table_bytes + L.ranges_bytes;
+  char* scratch = ws + L.table_bytes + L.ranges_bytes + L.tasks_bytes;
 
-  // host staging of the table and the ranges; thread-local so concurrent
-  // calls on different threads do not share it
+  // host staging of the table, the ranges and the reduction runs;
+  // thread-local so concurrent calls on different threads do not share it
   thread_local std::vector<char> host;
-  host.assign(L.table_bytes + L.ranges_bytes, 0);
+  host.assign(L.table_bytes + L.ranges_bytes + L.tasks_bytes, 0);
   std::vector<DevMat> mats(count);
   int64_t unit0 = 0;
+  bool any_nv = false, any_fp8 = false, all_aligned = true;
   for (int i = 0; i < count; ++i) {
     const wq_matrix& d = descs[i];
     mats[i] = dev_mat(d.fmt, d.w, d.scales, d.global_scale, d.x, d.y, d.M, d.K, L.splits[i],
                       scratch + L.scratch_off[i], N, unit0);
     unit0 += (int64_t)L.splits[i].nchunks * L.splits[i].ntiles;
-  }
-  const std::vector<WgRange> ranges = balance(descs, count, L);
-  std::memcpy(host.data(), mats.data(), sizeof(DevMat) * count);
-  std::memcpy(host.data() + L.table_bytes, ranges.data(), sizeof(WgRange) * ranges.size());
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
-    return WQ_ERROR_LAUNCH;
-  bool any_nv = false, any_fp8 = false, all_aligned = true;
-  for (int i = 0; i < count; ++i) {
-    if (descs[i].fmt == kFmtNvfp4) {
+    if (d.fmt == kFmtNvfp4) {
       any_nv = true;
-      all_aligned = all_aligned && descs[i].K % 64 == 0;
+      all_aligned = all_aligned && d.K % 64 == 0;
     } else {
       any_fp8 = true;
     }
   }
-  const int mode = any_nv && any_fp8 ? kModeMixed : any_fp8 ? kModeFp8 : all_aligned ? kModeNvfp4Aligned : kModeNvfp4;
+  const std::vector<WgRange> ranges = balance(descs, count, L);
+  std::memcpy(host.data(), mats.data(), sizeof(DevMat) * count);
+  std::memcpy(host.data() + L.table_bytes, ranges.data(), sizeof(WgRange) * ranges.size());
+  if (!L.tasks.empty())
+    std::memcpy(host.data() + L.table_bytes + L.ranges_bytes, L.tasks.data(), sizeof(ReduceTask) * L.tasks.size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+    return WQ_ERROR_LAUNCH;
+  plan->workspace = workspace;
+  plan->workspace_bytes = workspace_bytes;
+  plan->count = count;
+  plan->N = N;
+  plan->mode = any_nv && any_fp8 ? kModeMixed : any_fp8 ? kModeFp8 : all_aligned ? kModeNvfp4Aligned : kModeNvfp4;
+  plan->grid = L.grid;
+  plan->ranges_offset = L.table_bytes;
+  plan->reduce_offset = L.table_bytes + L.ranges_bytes;
+  plan->reduce_runs = (int32_t)L.tasks.size();
+  return WQ_SUCCESS;
+}
+
+wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {
+  if (!plan || !plan->workspace || plan->N < 1 || plan->N > 8 || plan->grid < 1 || plan->count < 1 ||
+      plan->mode < kModeNvfp4Aligned || plan->mode > kModeMixed || plan->ranges_offset >= plan->workspace_bytes ||
+      plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes))
+    return WQ_ERROR_INVALID_VALUE;
+  const char* ws = static_cast<const char*>(plan->workspace);
   const DevMat none{};
-  const hipError_t e = launch_stream(N, mode, reinterpret_cast<const DevMat*>(ws),
-                                     reinterpret_cast<const WgRange*>(ws + L.table_bytes), none, L.grid,
-                                     lds_bytes_for(N), s);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_stream(plan->N, plan->mode, reinterpret_cast<const DevMat*>(ws),
+                               reinterpret_cast<const WgRange*>(ws + plan->ranges_offset), none, plan->grid,
+                               lds_bytes_for(plan->N), s);
+  if (e == hipSuccess && plan->reduce_runs > 0)
+    e = launch_reduce(reinterpret_cast<const DevMat*>(ws), reinterpret_cast<const ReduceTask*>(ws + plan->reduce_offset),
+                      none, plan->reduce_runs, plan->N, s);
   return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+wq_status wq_verify_pass(const wq_matrix* descs, int count, int N, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  wq_verify_plan plan;
+  wq_status st = wq_verify_prepare(descs, count, N, workspace, workspace_bytes, stream, &plan);
+  if (st != WQ_SUCCESS) return st;
+  return wq_verify_launch(&plan, stream);
 }
 
 }  // extern "C"

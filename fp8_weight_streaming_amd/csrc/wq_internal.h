@@ -38,7 +38,6 @@ struct DevMat {
   const uint16_t* x;  // BF16 [N][K]
   float* y;           // FP32 [N][M]
   float* part;        // split-K partial sums [nchunks][N][M] (null if nchunks == 1)
-  unsigned* cnt;      // split-K arrival counters [ntiles] (null if nchunks == 1)
   float g;            // NVFP4 per-tensor scale
   int fmt, M, K;
   int kc;             // K chunk length (multiple of the format's segment)
@@ -54,6 +53,15 @@ struct WgRange {
   int32_t pad;
 };
 
+// One run of outputs of a split matrix for reduce_kernel.
+struct ReduceTask {
+  int64_t begin;  // first output index (n * M + m)
+  int32_t mat;
+  int32_t count;  // outputs in the run (<= kReduceRun)
+};
+constexpr int kReduceThreads = 256;
+constexpr int kReduceRun = 4096;
+
 // Kernel variants: which unit bodies a launch contains.
 constexpr int kModeNvfp4Aligned = 0;  // NVFP4 only, K % 64 == 0 for every matrix
 constexpr int kModeNvfp4 = 1;         // NVFP4 only, any K % 32 == 0
@@ -62,6 +70,8 @@ constexpr int kModeMixed = 3;         // both formats
 
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);
+hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevMat& one, int grid, int N,
+                         hipStream_t stream);
 
 }  // namespace wq
 

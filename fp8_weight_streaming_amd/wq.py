@@ -49,6 +49,13 @@ class WqMatrix(ctypes.Structure):
                 ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
+class WqVerifyPlan(ctypes.Structure):
+    _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("count", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("mode", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("ranges_offset", ctypes.c_size_t), ("reduce_offset", ctypes.c_size_t),
+                ("reduce_runs", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _S = ctypes.c_size_t
@@ -67,8 +74,21 @@ _lib.wq_verify_workspace_bytes.argtypes = [ctypes.POINTER(WqMatrix), _I, _I]
 _lib.wq_verify_pass.restype = _I
 _lib.wq_verify_pass.argtypes = [ctypes.POINTER(WqMatrix), _I, _I, _P, _S, _P]
 
-EXPORTED = ["wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4",
-            "wq_gemm_fp8row", "wq_verify_workspace_bytes", "wq_verify_pass"]
+_lib.wq_verify_prepare.restype = _I
+_lib.wq_verify_prepare.argtypes = [ctypes.POINTER(WqMatrix), _I, _I, _P, _S, _P, ctypes.POINTER(WqVerifyPlan)]
+_lib.wq_verify_launch.restype = _I
+_lib.wq_verify_launch.argtypes = [ctypes.POINTER(WqVerifyPlan), _P]
+
+_lib.wq_probe_sink_words.restype = _S
+_lib.wq_probe_sink_words.argtypes = []
+_lib.wq_probe_read.restype = _I
+_lib.wq_probe_read.argtypes = [_P, _S, _P, _P]
+_lib.wq_probe_copy.restype = _I
+_lib.wq_probe_copy.argtypes = [_P, _P, _S, _P]
+
+EXPORTED = ["wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
+            "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
+            "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
 
 def lib() -> ctypes.CDLL:
@@ -186,10 +206,33 @@ def wq_verify_pass(mats: Sequence[Matrix], N: int, workspace, stream=None, works
     _check(_lib.wq_verify_pass(arr, len(mats), N, _ptr(workspace), wsb, _stream(stream)), "wq_verify_pass")
 
 
-def descriptor_array(mats: Sequence[Matrix]):
-    """The ctypes descriptor array (for callers that reuse it across calls)."""
-    return _descs(mats)
+def wq_verify_prepare(mats: Sequence[Matrix], N: int, workspace, stream=None,
+                      workspace_bytes: Optional[int] = None) -> WqVerifyPlan:
+    """Write the pass's device table into `workspace`; returns the plan."""
+    arr = _descs(mats)
+    plan = WqVerifyPlan()
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_verify_prepare(arr, len(mats), N, _ptr(workspace), wsb, _stream(stream), ctypes.byref(plan)),
+           "wq_verify_prepare")
+    return plan
 
 
-def verify_pass_raw(arr, count: int, N: int, workspace_ptr: int, workspace_bytes: int, stream: int):
-    _check(_lib.wq_verify_pass(arr, count, N, workspace_ptr, workspace_bytes, stream), "wq_verify_pass")
+def wq_probe_sink_words() -> int:
+    return int(_lib.wq_probe_sink_words())
+
+
+def wq_probe_read(src, sink, stream=None, nbytes: Optional[int] = None):
+    """Stream `src` (device tensor) once with the weight stream's loads."""
+    nb = _nbytes(src) if nbytes is None else nbytes
+    _check(_lib.wq_probe_read(_ptr(src), nb, _ptr(sink), _stream(stream)), "wq_probe_read")
+
+
+def wq_probe_copy(src, dst, stream=None, nbytes: Optional[int] = None):
+    """Copy `src` to `dst` (device tensors of equal size)."""
+    nb = _nbytes(src) if nbytes is None else nbytes
+    _check(_lib.wq_probe_copy(_ptr(src), _ptr(dst), nb, _stream(stream)), "wq_probe_copy")
+
+
+def wq_verify_launch(plan: WqVerifyPlan, stream=None):
+    """Launch a prepared pass (kernel launch only)."""
+    _check(_lib.wq_verify_launch(ctypes.byref(plan), _stream(stream)), "wq_verify_launch")

@@ -30,12 +30,11 @@
  *    workbench" asks for the same bits on a repeat).  How K is split
  *    depends only on (M, K) and the device, never on N.
  *  - Workspace: some shapes split K across workgroups and need scratch
- *    memory (partial sums and per-tile arrival counters).  Query its size
- *    with the matching *_workspace_bytes call; pass a device buffer at
- *    least that large (16-byte aligned), or NULL/0 when the query returns
- *    0.  The buffer must be zero-filled before its first use with this
- *    library; every completed call leaves its counters at zero again, so
- *    a workspace can be reused by later calls of any shape.  Calls that
+ *    memory for the chunks' partial sums (added in chunk order by a second,
+ *    small kernel on the same stream).  Query its size with the matching
+ *    *_workspace_bytes call; pass a device buffer at least that large
+ *    (16-byte aligned), or NULL/0 when the query returns 0.  Its contents
+ *    need no initialization and are scratch after the call.  Calls that
  *    share one workspace must not overlap in time (same stream is fine).
  *  - Threading: the library keeps no state besides a per-device cache of
  *    the compute-unit count; calls are reentrant on different streams with
@@ -141,6 +140,48 @@ size_t wq_verify_workspace_bytes(const wq_matrix* descs, int count, int N);
  * they agree to FP32 rounding of the sums. */
 wq_status wq_verify_pass(const wq_matrix* descs, int count, int N,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* A verify pass split in two, for callers that run the same pass many
+ * times (every decode round of an engine) or capture it in a HIP graph:
+ * wq_verify_prepare validates the descriptors and writes the device-side
+ * table into `workspace` (one asynchronous host-to-device copy on
+ * `stream`), filling `plan`; wq_verify_launch then only launches the
+ * kernel and can be called any number of times, on any stream ordered
+ * after the copy, for as long as the workspace and every matrix buffer
+ * stay alive and unchanged in place.  wq_verify_pass is prepare + launch.
+ * The plan's fields are owned by the library; callers only keep it. */
+typedef struct wq_verify_plan {
+  void* workspace;
+  size_t workspace_bytes;
+  int32_t count;
+  int32_t N;
+  int32_t mode;
+  int32_t grid;
+  size_t ranges_offset;
+  size_t reduce_offset;
+  int32_t reduce_runs;
+  int32_t reserved;
+} wq_verify_plan;
+
+wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            wq_verify_plan* plan);
+wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream);
+
+/* Measurement kernels (not part of the product; they price it).  The crit
+ * README's Eval turns the GPU's measured bandwidth into a floor for each
+ * kernel, and the NInfer README ships a standalone bandwidth probe; these
+ * are the MI355X equivalents.
+ *  wq_probe_read: streams `bytes` (multiple of 16, src 16-byte aligned)
+ *    with the 16-byte non-temporal loads the weight stream uses, writing one
+ *    word per thread to `sink`, which must hold wq_probe_sink_words() words.
+ *  wq_probe_copy: copies `bytes` from src to dst (both 16-byte aligned,
+ *    not overlapping): a kernel that reads and writes exactly `bytes`, for
+ *    scaling hardware byte counters.
+ * Both only enqueue on `stream`. */
+size_t wq_probe_sink_words(void);
+wq_status wq_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+wq_status wq_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }
