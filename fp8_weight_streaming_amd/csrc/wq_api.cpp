@@ -60,7 +60,8 @@ struct Split {
   int ntiles = 0;
 };
 
-int seg_k(int fmt) { return fmt == kFmtNvfp4 ? 128 : 64; }
+int seg_k(int fmt) { return fmt == kFmtNvfp4Tiled ? kTileStepK : fmt == kFmtNvfp4 ? 128 : 64; }
+bool is_nvfp4(int fmt) { return fmt == kFmtNvfp4 || fmt == kFmtNvfp4Tiled; }
 
 Split make_split(int fmt, int M, int K, int kc) {
   Split s;
@@ -109,16 +110,18 @@ Split gemm_split(int fmt, int M, int K, int cus) {
 
 // ---- validation ------------------------------------------------------------------
 wq_status check_shape(int fmt, int M, int K, int N) {
-  if (fmt != kFmtNvfp4 && fmt != kFmtFp8Row) return WQ_ERROR_INVALID_VALUE;
+  if (fmt != kFmtNvfp4 && fmt != kFmtFp8Row && fmt != kFmtNvfp4Tiled) return WQ_ERROR_INVALID_VALUE;
   if (N < 1 || N > 8 || M < 1 || K < 1) return WQ_ERROR_INVALID_VALUE;
-  const int mult = fmt == kFmtNvfp4 ? 32 : 16;
+  const int mult = is_nvfp4(fmt) ? 32 : 16;
   if (K % mult != 0 || K > (1 << 24)) return WQ_ERROR_UNSUPPORTED_SHAPE;
-  const uint64_t wbytes = fmt == kFmtNvfp4 ? (uint64_t)M * (uint64_t)(K / 2) : (uint64_t)M * (uint64_t)K;
+  const uint64_t wbytes = is_nvfp4(fmt) ? (uint64_t)M * (uint64_t)(K / 2) : (uint64_t)M * (uint64_t)K;
   if (wbytes >= (1ull << 40)) return WQ_ERROR_UNSUPPORTED_SHAPE;
   return WQ_SUCCESS;
 }
 
-wq_status check_ptrs(const void* w, const void* s, const void* x, const void* y) {
+// Tiled NVFP4 carries its scales inside `w`; `s` is not used for it.
+wq_status check_ptrs(int fmt, const void* w, const void* s, const void* x, const void* y) {
+  if (fmt == kFmtNvfp4Tiled) s = w;
   if (!w || !s || !x || !y) return WQ_ERROR_INVALID_VALUE;
   if (!aligned16(w) || !aligned16(s) || !aligned16(x) || !aligned16(y)) return WQ_ERROR_MISALIGNED;
   return WQ_SUCCESS;
@@ -134,7 +137,7 @@ DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x
                const Split& sp, char* scratch, int N, int64_t unit0) {
   DevMat d{};
   d.w = static_cast<const uint8_t*>(w);
-  d.s = fmt == kFmtNvfp4 ? static_cast<const uint8_t*>(s) : nullptr;
+  d.s = fmt == kFmtNvfp4 ? static_cast<const uint8_t*>(s) : nullptr;  // tiled: inside w
   d.rs = fmt == kFmtFp8Row ? static_cast<const float*>(s) : nullptr;
   d.x = x;
   d.y = y;
@@ -154,7 +157,7 @@ wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x
                int N, void* ws, size_t ws_bytes, void* stream) {
   wq_status st = check_shape(fmt, M, K, N);
   if (st != WQ_SUCCESS) return st;
-  st = check_ptrs(w, s, x, y);
+  st = check_ptrs(fmt, w, s, x, y);
   if (st != WQ_SUCCESS) return st;
   if (ws && !aligned16(ws)) return WQ_ERROR_MISALIGNED;
   const int cus = current_cus();
@@ -165,7 +168,9 @@ wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x
   const DevMat one = dev_mat(fmt, w, s, g, x, y, M, K, sp, static_cast<char*>(ws), N, 0);
   const int64_t units = (int64_t)sp.nchunks * sp.ntiles;
   const int grid = (int)std::min<int64_t>(cus, units);
-  const int mode = fmt == kFmtFp8Row ? kModeFp8 : (K % 64 == 0 ? kModeNvfp4Aligned : kModeNvfp4);
+  const int mode = fmt == kFmtFp8Row ? kModeFp8
+                   : fmt == kFmtNvfp4Tiled ? kModeNvfp4Tiled
+                   : (K % 64 == 0 ? kModeNvfp4Aligned : kModeNvfp4);
   hipError_t e = launch_stream(N, mode, nullptr, nullptr, one, grid, lds_bytes_for(N),
                                static_cast<hipStream_t>(stream));
   if (e == hipSuccess && sp.nchunks > 1)
@@ -190,7 +195,7 @@ wq_status check_descs(const wq_matrix* descs, int count, int N) {
     const wq_matrix& d = descs[i];
     wq_status st = check_shape(d.fmt, d.M, d.K, N);
     if (st != WQ_SUCCESS) return st;
-    st = check_ptrs(d.w, d.scales, d.x, d.y);
+    st = check_ptrs(d.fmt, d.w, d.scales, d.x, d.y);
     if (st != WQ_SUCCESS) return st;
   }
   return WQ_SUCCESS;
@@ -232,7 +237,7 @@ std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout
   auto unit_cost = [&](int i, int c) {
     const Split& sp = L.splits[i];
     const int klen = std::min(sp.kc, descs[i].K - c * sp.kc);
-    const double bytes_per_k = descs[i].fmt == kFmtNvfp4 ? 16.0 * 0.5625 : 16.0;
+    const double bytes_per_k = is_nvfp4(descs[i].fmt) ? 16.0 * 0.5625 : 16.0;
     return bytes_per_k * klen + 4096.0;
   };
   double total = 0.0;
@@ -312,6 +317,11 @@ wq_status wq_gemm_nvfp4(const uint8_t* codes, const uint8_t* scales, float globa
   return gemm(kFmtNvfp4, codes, scales, global_scale, x, y, M, K, N, workspace, workspace_bytes, stream);
 }
 
+wq_status wq_gemm_nvfp4_tiled(const uint8_t* tiled, float global_scale, const uint16_t* x, float* y, int M, int K,
+                              int N, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm(kFmtNvfp4Tiled, tiled, nullptr, global_scale, x, y, M, K, N, workspace, workspace_bytes, stream);
+}
+
 wq_status wq_gemm_fp8row(const uint8_t* w, const float* row_scale, const uint16_t* x, float* y, int M, int K,
                          int N, void* workspace, size_t workspace_bytes, void* stream) {
   return gemm(kFmtFp8Row, w, row_scale, 1.0f, x, y, M, K, N, workspace, workspace_bytes, stream);
@@ -344,7 +354,7 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
   host.assign(L.table_bytes + L.ranges_bytes + L.tasks_bytes, 0);
   std::vector<DevMat> mats(count);
   int64_t unit0 = 0;
-  bool any_nv = false, any_fp8 = false, all_aligned = true;
+  bool any_nv = false, any_fp8 = false, any_tiled = false, all_aligned = true;
   for (int i = 0; i < count; ++i) {
     const wq_matrix& d = descs[i];
     mats[i] = dev_mat(d.fmt, d.w, d.scales, d.global_scale, d.x, d.y, d.M, d.K, L.splits[i],
@@ -353,6 +363,8 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
     if (d.fmt == kFmtNvfp4) {
       any_nv = true;
       all_aligned = all_aligned && d.K % 64 == 0;
+    } else if (d.fmt == kFmtNvfp4Tiled) {
+      any_tiled = true;
     } else {
       any_fp8 = true;
     }
@@ -369,7 +381,11 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
   plan->workspace_bytes = workspace_bytes;
   plan->count = count;
   plan->N = N;
-  plan->mode = any_nv && any_fp8 ? kModeMixed : any_fp8 ? kModeFp8 : all_aligned ? kModeNvfp4Aligned : kModeNvfp4;
+  const int kinds = (int)any_nv + (int)any_fp8 + (int)any_tiled;
+  plan->mode = kinds > 1 ? kModeMixed
+               : any_fp8 ? kModeFp8
+               : any_tiled ? kModeNvfp4Tiled
+               : all_aligned ? kModeNvfp4Aligned : kModeNvfp4;
   plan->grid = L.grid;
   plan->ranges_offset = L.table_bytes;
   plan->reduce_offset = L.table_bytes + L.ranges_bytes;
@@ -379,7 +395,7 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
 
 wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {
   if (!plan || !plan->workspace || plan->N < 1 || plan->N > 8 || plan->grid < 1 || plan->count < 1 ||
-      plan->mode < kModeNvfp4Aligned || plan->mode > kModeMixed || plan->ranges_offset >= plan->workspace_bytes ||
+      plan->mode < kModeNvfp4Aligned || plan->mode > kModeNvfp4Tiled || plan->ranges_offset >= plan->workspace_bytes ||
       plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes))
     return WQ_ERROR_INVALID_VALUE;
   const char* ws = static_cast<const char*>(plan->workspace);

@@ -10,6 +10,15 @@ namespace wq {
 
 constexpr int kFmtNvfp4 = 0;
 constexpr int kFmtFp8Row = 1;
+constexpr int kFmtNvfp4Tiled = 2;
+
+// Tiled NVFP4 storage: blocks of 16 rows x 256 k, each 2048 bytes of codes
+// (two 1 KB halves in MFMA lane order) followed by 256 bytes of block
+// scales (grouped by the scale parity each lane applies).
+constexpr int kTileRows = 16;
+constexpr int kTileStepK = 256;
+constexpr int kTileCodeBytes = 2048;
+constexpr int kTileBlockBytes = 2304;
 
 // One persistent workgroup per CU: 16 waves of 64 lanes.
 constexpr int kThreads = 1024;
@@ -19,20 +28,28 @@ constexpr int kPrefetch = 8;
 // Shallower pipeline for the variants that also carry unaligned-scale or
 // mixed-format code, to stay within 128 VGPRs.
 constexpr int kPrefetchGeneric = 4;
+// Steps (2304-byte blocks) in flight per lane for tiled NVFP4.
+constexpr int kPrefetchTiled = 4;
 // Largest K chunk whose N <= 8 BF16 columns are staged in LDS at once.
 constexpr int kKcMax = 8704;
 // LDS: X chunk as (k/8, n) pieces of 16 bytes, then a zero block read by the
 // lanes whose A-operand slots are structurally zero.
 template <int N>
 __host__ __device__ constexpr uint32_t kZeroOffset() { return (uint32_t)kKcMax * 2u * N; }
+// The zero block must cover the largest offset an idle lane adds to it:
+// tiled NVFP4 reads at up to 256N (second half) + 3*64N (MFMA step) + 16.
 template <int N>
-__host__ __device__ constexpr uint32_t kZeroBytes() { return 256u * N; }
-constexpr uint32_t lds_bytes_for(int n) { return (uint32_t)kKcMax * 2u * n + 256u * n; }
+__host__ __device__ constexpr uint32_t kZeroBytes() { return 512u * N; }
+constexpr uint32_t lds_bytes_for(int n) { return (uint32_t)kKcMax * 2u * n + 512u * n; }
 constexpr uint32_t kMaxLdsBytes = lds_bytes_for(8);
+// idle-lane reads: tiled NVFP4 at 256N + 192N + 16, plain NVFP4 at 192N + 16,
+// FP8-row at 16N + 16 bytes past the zero block's start
+static_assert(kZeroBytes<1>() >= 448u * 1 + 16u && kZeroBytes<8>() >= 448u * 8 + 16u, "zero block too small");
+static_assert(kMaxLdsBytes <= 160u * 1024u, "LDS budget exceeded");
 
 // Device-side descriptor of one matrix (built on the host).
 struct DevMat {
-  const uint8_t* w;   // NVFP4 codes [M][K/2] or FP8 codes [M][K]
+  const uint8_t* w;   // NVFP4 codes [M][K/2], FP8 codes [M][K] or tiled NVFP4 blocks
   const uint8_t* s;   // NVFP4 block scales [M][K/16] (null for FP8-row)
   const float* rs;    // FP8 row scales [M] (null for NVFP4)
   const uint16_t* x;  // BF16 [N][K]
@@ -66,7 +83,8 @@ constexpr int kReduceRun = 4096;
 constexpr int kModeNvfp4Aligned = 0;  // NVFP4 only, K % 64 == 0 for every matrix
 constexpr int kModeNvfp4 = 1;         // NVFP4 only, any K % 32 == 0
 constexpr int kModeFp8 = 2;           // FP8-row only
-constexpr int kModeMixed = 3;         // both formats
+constexpr int kModeMixed = 3;         // any formats
+constexpr int kModeNvfp4Tiled = 4;    // tiled NVFP4 only
 
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);

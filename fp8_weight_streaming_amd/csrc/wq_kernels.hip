@@ -257,6 +257,87 @@ __device__ void nvfp4_unit(const DevMat& mt, int chunk, int tile, const char* ld
   finish_tile<N>(mt, chunk, tile, sum, mt.g);
 }
 
+// ---- one tiled-NVFP4 unit --------------------------------------------------
+// Same arithmetic as nvfp4_unit, on weights stored by wq_nvfp4_tile: a step
+// of 256 k is one 2304-byte block per 16-row tile, so each lane's loads are
+// 16 bytes of one contiguous 1 KB (codes, twice) plus 8 bytes of one
+// contiguous 256 B (scales), with the codes already in the order the MFMA
+// B operand wants and the scales already split by parity.
+template <int N, int PF>
+__device__ void nvfp4_tiled_unit(const DevMat& mt, int chunk, int tile, const char* lds) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int k0 = chunk * mt.kc;
+  const int klen = min(mt.kc, mt.K - k0);
+  const int nst = (klen + kTileStepK - 1) / kTileStepK;
+  const uint64_t steps_per_row = (uint64_t)(mt.K + kTileStepK - 1) / kTileStepK;
+  const uint64_t start = ((uint64_t)tile * steps_per_row + (uint64_t)(k0 / kTileStepK)) * kTileBlockBytes;
+  const uint64_t total = (uint64_t)mt.ntiles * steps_per_row * kTileBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(mt.w + start, total - start);
+  const uint32_t vc = 16u * lane;
+  const uint32_t vs = (uint32_t)kTileCodeBytes + 8u * (uint32_t)(((lane >> 5) << 4) + c);
+
+  const bool active = ((c >> 3) == (g >> 1)) && ((c & 7) < N);
+  const uint32_t xoff = active ? (uint32_t)((g * N + (c & 7)) * 16) : kZeroOffset<N>();
+  const uint32_t xstep = active ? 512u * N : 0u;
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  u32x4 c0[PF], c1[PF];
+  u32x2 sw[PF];
+  const int last = nst - 1;
+  auto load = [&](int st, int slot) {
+    const uint32_t b = (uint32_t)min(st, last) * (uint32_t)kTileBlockBytes;
+    c0[slot] = bload16(rw, b + vc);
+    c1[slot] = bload16(rw, b + 1024u + vc);
+    sw[slot] = bload8(rw, b + vs);
+  };
+  auto half = [&](const u32x4& e, uint32_t sb, uint32_t xo) {
+    const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
+    const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, true);
+    const float stv[4] = {s01.x, s01.y, s23.x, s23.y};
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = lds_read16(lds, xo + t * 64u * N);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b[t] = e2m1x8_to_bf16(e[t]);
+    f32x4 part[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], b[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(stv[t], part[t][r], acc[r]);
+  };
+  auto compute = [&](int slot, int st) {
+    const uint32_t xo = xoff + (uint32_t)st * xstep;
+    half(c0[slot], sw[slot].x, xo);
+    half(c1[slot], sw[slot].y, xo + 256u * N);
+  };
+
+#pragma unroll
+  for (int i = 0; i < PF; ++i) load(i, i);
+  int s0 = 0;
+  for (; s0 + PF <= nst; s0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      compute(i, s0 + i);
+      load(s0 + i + PF, i);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (s0 + i < nst) compute(i, s0 + i);
+
+  float sum[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u32x2 sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
+    sum[r] = acc[r] + __uint_as_float(sw2.y);
+  }
+  finish_tile<N>(mt, chunk, tile, sum, mt.g);
+}
+
 // ---- one FP8-row unit ------------------------------------------------------
 template <int N, int PF>
 __device__ void fp8_unit(const DevMat& mt, int chunk, int tile, const char* lds) {
@@ -359,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const DevMat* __restri
     const int64_t run_end = min(u_end, mt.unit0 + (int64_t)(chunk + 1) * mt.ntiles);
     const int k0 = chunk * mt.kc;
     const int klen = min(mt.kc, mt.K - k0);
-    const int seg_k = mt.fmt == kFmtNvfp4 ? 128 : 64;
+    const int seg_k = mt.fmt == kFmtNvfp4Tiled ? kTileStepK : mt.fmt == kFmtNvfp4 ? 128 : 64;
     const int kc_pad = ((klen + seg_k - 1) / seg_k) * (seg_k / 8);
     __syncthreads();
     stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
@@ -372,9 +453,13 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const DevMat* __restri
         nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
       } else if constexpr (MODE == kModeFp8) {
         fp8_unit<N, kPrefetch>(mt, chunk, tile, lds);
+      } else if constexpr (MODE == kModeNvfp4Tiled) {
+        nvfp4_tiled_unit<N, kPrefetchTiled>(mt, chunk, tile, lds);
       } else {
         if (mt.fmt == kFmtNvfp4)
           nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
+        else if (mt.fmt == kFmtNvfp4Tiled)
+          nvfp4_tiled_unit<N, kPrefetchGeneric / 2>(mt, chunk, tile, lds);
         else
           fp8_unit<N, kPrefetchGeneric>(mt, chunk, tile, lds);
       }
@@ -407,7 +492,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const DevMat* __
     const int m = (int)(o % mt.M);
     float acc = 0.0f;
     for (int c = 0; c < mt.nchunks; ++c) acc += mt.part[c * plane + o];
-    const float scale = mt.fmt == kFmtNvfp4 ? mt.g : mt.rs[m];
+    // row scales exist only for FP8-row; both NVFP4 layouts use g
+    const float scale = mt.fmt == kFmtFp8Row ? mt.rs[m] : mt.g;
     mt.y[o] = scale * acc;
   }
 }
@@ -441,6 +527,7 @@ static hipError_t launch_n(int mode, const DevMat* mats, const WgRange* ranges, 
     case kModeNvfp4: return launch_nm<N, kModeNvfp4>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeFp8: return launch_nm<N, kModeFp8>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeMixed: return launch_nm<N, kModeMixed>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeNvfp4Tiled: return launch_nm<N, kModeNvfp4Tiled>(mats, ranges, one, grid, lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

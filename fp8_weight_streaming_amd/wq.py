@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libwq.so")
 
 WQ_FMT_NVFP4 = 0
 WQ_FMT_FP8ROW = 1
+WQ_FMT_NVFP4_TILED = 2
 
 STATUS_NAMES = {
     0: "WQ_SUCCESS",
@@ -86,7 +87,16 @@ _lib.wq_probe_read.argtypes = [_P, _S, _P, _P]
 _lib.wq_probe_copy.restype = _I
 _lib.wq_probe_copy.argtypes = [_P, _P, _S, _P]
 
-EXPORTED = ["wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
+_lib.wq_nvfp4_tiled_bytes.restype = _S
+_lib.wq_nvfp4_tiled_bytes.argtypes = [_I, _I]
+_lib.wq_nvfp4_tile.restype = _I
+_lib.wq_nvfp4_tile.argtypes = [_P, _P, _I, _I, _P, _P]
+_lib.wq_nvfp4_untile.restype = _I
+_lib.wq_nvfp4_untile.argtypes = [_P, _I, _I, _P, _P, _P]
+_lib.wq_gemm_nvfp4_tiled.restype = _I
+_lib.wq_gemm_nvfp4_tiled.argtypes = [_P, ctypes.c_float, _P, _P, _I, _I, _I, _P, _S, _P]
+
+EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
@@ -157,6 +167,38 @@ def wq_gemm_nvfp4(codes, scales, global_scale: float, x, y, workspace=None, stre
     wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     _check(_lib.wq_gemm_nvfp4(_ptr(codes), _ptr(scales), float(global_scale), _ptr(x), _ptr(y), M, K, N,
                               _ptr(workspace), wsb, _stream(stream)), "wq_gemm_nvfp4")
+
+
+def wq_nvfp4_tiled_bytes(M: int, K: int) -> int:
+    return int(_lib.wq_nvfp4_tiled_bytes(M, K))
+
+
+def wq_nvfp4_tile(codes, scales, tiled, stream=None, M: Optional[int] = None, K: Optional[int] = None):
+    """Permute plain NVFP4 codes/scales into the tiled layout (on the GPU)."""
+    if M is None:
+        M = codes.shape[0]
+    if K is None:
+        K = 2 * codes.shape[1]
+    _check(_lib.wq_nvfp4_tile(_ptr(codes), _ptr(scales), M, K, _ptr(tiled), _stream(stream)), "wq_nvfp4_tile")
+
+
+def wq_nvfp4_untile(tiled, codes, scales, stream=None, M: Optional[int] = None, K: Optional[int] = None):
+    """Inverse of wq_nvfp4_tile."""
+    if M is None:
+        M = codes.shape[0]
+    if K is None:
+        K = 2 * codes.shape[1]
+    _check(_lib.wq_nvfp4_untile(_ptr(tiled), M, K, _ptr(codes), _ptr(scales), _stream(stream)), "wq_nvfp4_untile")
+
+
+def wq_gemm_nvfp4_tiled(tiled, global_scale: float, x, y, M: int, K: int, workspace=None, stream=None,
+                        N: Optional[int] = None, workspace_bytes: Optional[int] = None):
+    """y[N, M] = x[N, K] . W^T for NVFP4 W in the tiled layout."""
+    if N is None:
+        N = x.shape[0]
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_gemm_nvfp4_tiled(_ptr(tiled), float(global_scale), _ptr(x), _ptr(y), M, K, N, _ptr(workspace),
+                                    wsb, _stream(stream)), "wq_gemm_nvfp4_tiled")
 
 
 def wq_gemm_fp8row(w, row_scale, x, y, workspace=None, stream=None, M: Optional[int] = None,

@@ -60,7 +60,7 @@ typedef enum wq_status {
   WQ_ERROR_DEVICE = 6             /* no current HIP device, or not a gfx950 device */
 } wq_status;
 
-enum { WQ_FMT_NVFP4 = 0, WQ_FMT_FP8ROW = 1 };
+enum { WQ_FMT_NVFP4 = 0, WQ_FMT_FP8ROW = 1, WQ_FMT_NVFP4_TILED = 2 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* wq_status_string(wq_status s);
@@ -97,6 +97,34 @@ wq_status wq_gemm_nvfp4(const uint8_t* codes, const uint8_t* scales, float globa
                         const uint16_t* x, float* y, int M, int K, int N,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Tiled NVFP4: the same codes and scales, permuted once at load time into
+ * the order the NVFP4 kernels stream (the card's section "Design", row
+ * "Weights", likewise keeps NVFP4 scales in a kernel-specific tile order).
+ * For T = ceil(M/16) row tiles and S = ceil(K/256) steps, block (t, s) is
+ * 2304 bytes at offset (t*S + s)*2304 and covers rows 16t..16t+15 and
+ * k = 256s..256s+255 (rows >= M and k >= K are zero codes with zero
+ * scales).  Inside it, with lane l = c + 16g (c = 0..15, g = 0..3),
+ * h = 0..1 and j = 0..3:
+ *   bytes [1024h + 16l + 4j, +4) = plain code bytes
+ *       [128s + 64h + 16j + 4g, +4) of row 16t + c;
+ *   byte 2048 + 8(16p + c) + 4h + j (p = 0..1) = the scale of row 16t + c
+ *       for scale block 16s + 8h + 2j + p.
+ * wq_nvfp4_tiled_bytes: size of the tiled buffer (0 for an invalid shape).
+ * wq_nvfp4_tile / wq_nvfp4_untile: convert on the GPU (enqueue only; all
+ *   buffers 16-byte aligned, shapes as for wq_gemm_nvfp4).  untile(tile(w))
+ *   reproduces codes and scales bit for bit.
+ * wq_gemm_nvfp4_tiled: the product on tiled weights; same results as
+ *   wq_gemm_nvfp4 on the plain weights (bit for bit when wq_gemm_split
+ *   reports the same split for WQ_FMT_NVFP4 and WQ_FMT_NVFP4_TILED). */
+size_t wq_nvfp4_tiled_bytes(int M, int K);
+wq_status wq_nvfp4_tile(const uint8_t* codes, const uint8_t* scales, int M, int K,
+                        uint8_t* tiled, void* stream);
+wq_status wq_nvfp4_untile(const uint8_t* tiled, int M, int K,
+                          uint8_t* codes, uint8_t* scales, void* stream);
+wq_status wq_gemm_nvfp4_tiled(const uint8_t* tiled, float global_scale,
+                              const uint16_t* x, float* y, int M, int K, int N,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Row-scaled FP8-E4M3 weights (the card's section "Model": projections and
  * output head stored or re-encoded as FP8 with one scale per output row).
  *   w         [M][K] uint8 E4M3 (FN) codes.
@@ -110,8 +138,10 @@ wq_status wq_gemm_fp8row(const uint8_t* w, const float* row_scale,
 
 /* One matrix of a verify pass (host-side descriptor).  For WQ_FMT_NVFP4,
  * `w` = codes, `scales` = block scales, `global_scale` used; for
- * WQ_FMT_FP8ROW, `w` = E4M3 codes, `scales` = the FP32 row scales
- * (reinterpreted), `global_scale` ignored.  x [N][K], y [N][M] as above. */
+ * WQ_FMT_NVFP4_TILED, `w` = the tiled buffer, `scales` unused (may be
+ * NULL), `global_scale` used; for WQ_FMT_FP8ROW, `w` = E4M3 codes,
+ * `scales` = the FP32 row scales (reinterpreted), `global_scale` ignored.
+ * x [N][K], y [N][M] as above. */
 typedef struct wq_matrix {
   int32_t fmt;
   int32_t M;
