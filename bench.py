@@ -7,7 +7,10 @@ o 5120x6144, gate+up 34816x5120, down 5120x17408}, every matrix NVFP4
 N cycled over 2, 4, 8 from one pass to the next, all 256 matrices in one
 persistent launch (wq_verify_launch of a prepared plan).  Inputs are
 seeded synthetic arrays (fp8_weight_streaming_amd.inputs), resident in HBM
-before the timed region.
+before the timed region.  The weights are streamed in the tiled NVFP4
+layout (the same bytes, permuted once at load time by wq_nvfp4_tile,
+outside the timed region); the plain row-major layout is timed too and
+reported under "plain_layout".
 
 Printed: ONE JSON line with the metric (achieved HBM GB/s over the timed
 passes, algorithmic bytes per pass / pass time), the per-N breakdown, a
@@ -202,19 +205,29 @@ def main():
         scales = torch.from_numpy(d.scales).to(dev)
         x = torch.from_numpy(d.x.view(np.int16)).to(dev)
         y = torch.zeros((NMAX, spec.M), dtype=torch.float32, device=dev)
-        mats_dev.append((codes, scales, x, y))
+        tiled = torch.empty(wq.wq_nvfp4_tiled_bytes(spec.M, spec.K), dtype=torch.uint8, device=dev)
+        wq.wq_nvfp4_tile(codes, scales, tiled, stream)
+        mats_dev.append((codes, scales, x, y, tiled))
     torch.cuda.synchronize()
-    print("[bench] uploaded %.2f GB" % (sum(c.numel() + s.numel() for c, s, _, _ in mats_dev) / 1e9),
+    print("[bench] uploaded %.2f GB and tiled it" % (sum(c.numel() + s.numel() for c, s, _, _, _ in mats_dev) / 1e9),
           file=sys.stderr, flush=True)
 
-    plans, keep = {}, []
-    for N in N_CYCLE:
-        mats = [wq.Matrix(wq.WQ_FMT_NVFP4, s.M, s.K, c, sc, x[:N], y[:N], wl.g)
-                for s, (c, sc, x, y) in zip(wl.matrices, mats_dev)]
-        nbytes = wq.wq_verify_workspace_bytes(mats, N)
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-        plans[N] = wq.wq_verify_prepare(mats, N, ws, stream)
-        keep.append((mats, ws))
+    def make_plans(fmt):
+        plans = {}
+        for N in N_CYCLE:
+            if fmt == wq.WQ_FMT_NVFP4_TILED:
+                mats = [wq.Matrix(fmt, s.M, s.K, t, None, x[:N], y[:N], wl.g)
+                        for s, (c, sc, x, y, t) in zip(wl.matrices, mats_dev)]
+            else:
+                mats = [wq.Matrix(fmt, s.M, s.K, c, sc, x[:N], y[:N], wl.g)
+                        for s, (c, sc, x, y, t) in zip(wl.matrices, mats_dev)]
+            ws = torch.zeros(wq.wq_verify_workspace_bytes(mats, N), dtype=torch.uint8, device=dev)
+            plans[N] = (wq.wq_verify_prepare(mats, N, ws, stream), ws)
+        return plans
+
+    plans_t = make_plans(wq.WQ_FMT_NVFP4_TILED)
+    plans_p = make_plans(wq.WQ_FMT_NVFP4)
+    plans = {N: p for N, (p, _) in plans_t.items()}
     torch.cuda.synchronize()
 
     # attainable read rate (probe) and a copy of known size (counter scale)
@@ -276,10 +289,25 @@ def main():
     traffic, traffic_kv = read_traffic()
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / PEAK_GBPS, "traffic": traffic,
-                "kernel": "wq::stream_kernel<N, mode 0> (one launch per verify pass)",
+                "kernel": "wq::stream_kernel<N, tiled-NVFP4 mode> + wq::reduce_kernel (one verify pass)",
                 "avg_launch_us": kernel_s / steps * 1e6,
                 "algorithmic_bytes_per_launch_mean": total_bytes / steps,
                 "probe_read_gbps": probe_gbps, "frac_of_probe": achieved / probe_gbps}
+
+    # the plain row-major layout, timed the same way (reported only)
+    plain = {}
+    for N in N_CYCLE:
+        p = plans_p[N][0]
+        for _ in range(2):
+            wq.wq_verify_launch(p, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(9):
+            wq.wq_verify_launch(p, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / 9 * 1e3
+        plain[str(N)] = {"us_per_pass": us, "gbps": bytes_n[N] / us / 1e3}
 
     # parity: sampled rows of every matrix at every N against the oracle
     import oracle
@@ -326,6 +354,7 @@ def main():
                    "pct_of_8TBps": 100 * value / PEAK_GBPS,
                    "us_per_pass": wall_s / steps * 1e6},
         "per_n": per_n,
+        "plain_layout": plain,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
