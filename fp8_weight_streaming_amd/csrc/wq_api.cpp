@@ -87,7 +87,7 @@ Split verify_split(int fmt, int M, int K) {
 // be taken, since it costs partial-sum traffic.
 Split gemm_split(int fmt, int M, int K, int cus) {
   const int sk = seg_k(fmt);
-  const int64_t slots = (int64_t)cus * kWaves;
+  const int64_t slots = (int64_t)cus * waves_for_mode(fmt == kFmtNvfp4Tiled ? kModeNvfp4Tiled : kModeNvfp4);
   const int64_t ntiles = ceil_div(M, 16);
   const int nmin = (int)ceil_div(K, kKcMax);
   const int nmax = std::max(nmin, (int)std::min<int64_t>(64, ceil_div(K, sk)));
@@ -116,6 +116,12 @@ wq_status check_shape(int fmt, int M, int K, int N) {
   if (K % mult != 0 || K > (1 << 24)) return WQ_ERROR_UNSUPPORTED_SHAPE;
   const uint64_t wbytes = is_nvfp4(fmt) ? (uint64_t)M * (uint64_t)(K / 2) : (uint64_t)M * (uint64_t)K;
   if (wbytes >= (1ull << 40)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  // outputs are addressed with 32-bit buffer offsets below 2 GiB
+  if ((uint64_t)N * (uint64_t)M * 4u >= (1ull << 31)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  // a tiled matrix is addressed with 32-bit buffer offsets
+  if (fmt == kFmtNvfp4Tiled &&
+      (uint64_t)((M + kTileRows - 1) / kTileRows) * ((K + kTileStepK - 1) / kTileStepK) * kTileBlockBytes >= (1ull << 32))
+    return WQ_ERROR_UNSUPPORTED_SHAPE;
   return WQ_SUCCESS;
 }
 

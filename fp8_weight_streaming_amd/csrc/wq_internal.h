@@ -20,17 +20,21 @@ constexpr int kTileStepK = 256;
 constexpr int kTileCodeBytes = 2048;
 constexpr int kTileBlockBytes = 2304;
 
-// One persistent workgroup per CU: 16 waves of 64 lanes.
+// One persistent workgroup per CU: 16 waves of 64 lanes (8 waves with twice
+// the registers each for the tiled-NVFP4 kernel, whose ring spans tiles).
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kThreadsTiled = 512;
 // Segments (64 bytes of one row per lane group of four lanes) in flight.
 constexpr int kPrefetch = 8;
 // Shallower pipeline for the variants that also carry unaligned-scale or
 // mixed-format code, to stay within 128 VGPRs.
 constexpr int kPrefetchGeneric = 4;
 // Steps (2304-byte blocks) in flight per lane for tiled NVFP4.
-constexpr int kPrefetchTiled = 4;
-// Largest K chunk whose N <= 8 BF16 columns are staged in LDS at once.
+constexpr int kPrefetchTiled = 6;
+// Largest K chunk whose N <= 8 BF16 columns are staged in LDS at once.  The
+// chunking does not depend on N, so column n of a result has the same bits
+// for every N > n.
 constexpr int kKcMax = 8704;
 // LDS: X chunk as (k/8, n) pieces of 16 bytes, then a zero block read by the
 // lanes whose A-operand slots are structurally zero.
@@ -85,6 +89,10 @@ constexpr int kModeNvfp4 = 1;         // NVFP4 only, any K % 32 == 0
 constexpr int kModeFp8 = 2;           // FP8-row only
 constexpr int kModeMixed = 3;         // any formats
 constexpr int kModeNvfp4Tiled = 4;    // tiled NVFP4 only
+
+template <int MODE>
+__host__ __device__ constexpr int threads_for_mode() { return MODE == kModeNvfp4Tiled ? kThreadsTiled : kThreads; }
+constexpr int waves_for_mode(int mode) { return (mode == kModeNvfp4Tiled ? kThreadsTiled : kThreads) / 64; }
 
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);

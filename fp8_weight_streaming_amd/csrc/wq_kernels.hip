@@ -64,6 +64,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
 }
 
+// Tiled NVFP4 reads every line whole within one wave instruction, so the
+// non-temporal policy is safe there and streams faster (6.0 vs 5.7 TB/s).
+constexpr int kAuxTiled = 2;
+__device__ __forceinline__ u32x4 bload16t(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAuxTiled));
+}
+__device__ __forceinline__ u32x2 bload8t(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kAuxTiled));
+}
+// Same, with base and size pinned to scalar registers (they are wave-uniform;
+// the pinning keeps the compiler from treating the resource as divergent).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, uint64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                           kRsrcWord3);
+}
+
+// Output stores of the tiled stream are written through to memory (system
+// scope: sc0 sc1).  With the weight loads non-temporal, write-back made the
+// dirty output lines leave the L2 later as evictions that cost the read
+// stream more (measured on MI355X: 5.7-6.1 TB/s write-back against
+// 5.9-6.3 TB/s write-through over the dense 64-layer pass).
+constexpr int kAuxOut = 17;
+__device__ __forceinline__ void bstore4(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kAuxOut);
+}
+// A buffer offset past every output buffer (outputs are < 2 GiB): the
+// hardware range check drops stores there.
+constexpr uint32_t kDropOffset = 0x80000000u;
+
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAuxStream));
 }
@@ -257,23 +290,33 @@ __device__ void nvfp4_unit(const DevMat& mt, int chunk, int tile, const char* ld
   finish_tile<N>(mt, chunk, tile, sum, mt.g);
 }
 
-// ---- one tiled-NVFP4 unit --------------------------------------------------
+// ---- a wave's tiled-NVFP4 tiles of one run ----------------------------------
 // Same arithmetic as nvfp4_unit, on weights stored by wq_nvfp4_tile: a step
 // of 256 k is one 2304-byte block per 16-row tile, so each lane's loads are
 // 16 bytes of one contiguous 1 KB (codes, twice) plus 8 bytes of one
 // contiguous 256 B (scales), with the codes already in the order the MFMA
 // B operand wants and the scales already split by parity.
+//
+// The wave takes the consecutive tiles [first, end) of one matrix and K
+// chunk (all nst steps long).  They lie back to back in memory, so the
+// wave's whole share is one sequential stream, and it is streamed as ONE
+// sequence of steps: the ring keeps PF steps in flight across tile
+// boundaries.
+
 template <int N, int PF>
-__device__ void nvfp4_tiled_unit(const DevMat& mt, int chunk, int tile, const char* lds) {
+__device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds) {
+  if (first >= end) return;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int k0 = chunk * mt.kc;
   const int klen = min(mt.kc, mt.K - k0);
   const int nst = (klen + kTileStepK - 1) / kTileStepK;
-  const uint64_t steps_per_row = (uint64_t)(mt.K + kTileStepK - 1) / kTileStepK;
-  const uint64_t start = ((uint64_t)tile * steps_per_row + (uint64_t)(k0 / kTileStepK)) * kTileBlockBytes;
-  const uint64_t total = (uint64_t)mt.ntiles * steps_per_row * kTileBlockBytes;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(mt.w + start, total - start);
+  const int cnt = (int)(end - first);
+  const int tile0 = (int)((first - mt.unit0) - (int64_t)chunk * mt.ntiles);
+  const uint32_t steps_per_row = (uint32_t)((mt.K + kTileStepK - 1) / kTileStepK);
+  const uint32_t base_step = (uint32_t)(k0 / kTileStepK);
+  const uint64_t total = (uint64_t)mt.ntiles * steps_per_row * kTileBlockBytes;  // < 2^32 (checked on the host)
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc_uniform(mt.w, total);
   const uint32_t vc = 16u * lane;
   const uint32_t vs = (uint32_t)kTileCodeBytes + 8u * (uint32_t)(((lane >> 5) << 4) + c);
 
@@ -284,12 +327,18 @@ __device__ void nvfp4_tiled_unit(const DevMat& mt, int chunk, int tile, const ch
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   u32x4 c0[PF], c1[PF];
   u32x2 sw[PF];
-  const int last = nst - 1;
-  auto load = [&](int st, int slot) {
-    const uint32_t b = (uint32_t)min(st, last) * (uint32_t)kTileBlockBytes;
-    c0[slot] = bload16(rw, b + vc);
-    c1[slot] = bload16(rw, b + 1024u + vc);
-    sw[slot] = bload8(rw, b + vs);
+
+  // next step to load: tile li, step lst (past the end: the last step again)
+  int li = 0, lst = 0;
+  auto load_next = [&](int slot) {
+    const bool past = li >= cnt;
+    const uint32_t ti = (uint32_t)(past ? cnt - 1 : li);
+    const uint32_t ts = (uint32_t)(past ? nst - 1 : lst);
+    const uint32_t b = (((uint32_t)tile0 + ti) * steps_per_row + base_step + ts) * kTileBlockBytes;
+    c0[slot] = bload16t(rw, b + vc);
+    c1[slot] = bload16t(rw, b + 1024u + vc);
+    sw[slot] = bload8t(rw, b + vs);
+    if (++lst == nst) { lst = 0; ++li; }
   };
   auto half = [&](const u32x4& e, uint32_t sb, uint32_t xo) {
     const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
@@ -309,33 +358,69 @@ __device__ void nvfp4_tiled_unit(const DevMat& mt, int chunk, int tile, const ch
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(stv[t], part[t][r], acc[r]);
   };
-  auto compute = [&](int slot, int st) {
-    const uint32_t xo = xoff + (uint32_t)st * xstep;
+  // Outputs: y (scaled by g) for an unsplit matrix, else this chunk's plane
+  // of the partial sums; lanes 0..31 hold n = nb + r, m = 16 * tile + c.
+  // Every step issues the same min(N, 4) stores; only on a tile's last step
+  // do their offsets point into the buffer, otherwise the range check drops
+  // them.  An equal count of memory operations on every step keeps the
+  // compiler's vmcnt waits exact across the epilogue (a conditional store
+  // makes it wait for everything).
+  constexpr int kStores = N < 4 ? N : 4;
+  const bool split = mt.nchunks > 1;
+  float* const obase = split ? mt.part + (size_t)chunk * N * mt.M : mt.y;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc_uniform(obase, (uint64_t)N * (uint64_t)mt.M * 4u);
+  const float oscale = split ? 1.0f : mt.g;
+  const int nb = 4 * (lane >> 4);
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t so[4] = {kDropOffset, kDropOffset, kDropOffset, kDropOffset};
+
+  // next step to compute: tile ci, step cst
+  int ci = 0, cst = 0;
+  auto compute_next = [&](int slot) {
+    const uint32_t xo = xoff + (uint32_t)cst * xstep;
     half(c0[slot], sw[slot].x, xo);
     half(c1[slot], sw[slot].y, xo + 256u * N);
+    const bool fin = cst == nst - 1;
+    if (fin) {
+      // lanes l and l+32 hold blocks 0 and 1 of the same (n, m): add in that order
+      const int m = (tile0 + ci) * 16 + c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
+        sum[r] = oscale * (acc[r] + __uint_as_float(p.y));
+        acc[r] = 0.f;
+        const bool live = lane < 32 && m < mt.M && nb + r < N;
+        so[r] = live ? (uint32_t)(((nb + r) * mt.M + m) * 4) : kDropOffset;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kStores; ++r) bstore4(sum[r], ro, fin ? so[r] : kDropOffset);
+    if (++cst == nst) { cst = 0; ++ci; }
   };
 
+  const int Q = cnt * nst;
+  // The prologue issues each step's memory operations in the order the
+  // loop does (the stores, here all dropped and each to its own offset so
+  // none is merged away, then the loads), so that at the loop header the
+  // count of operations after each slot's load is the same on entry and on
+  // the back edge and the vmcnt waits can be exact.
 #pragma unroll
-  for (int i = 0; i < PF; ++i) load(i, i);
-  int s0 = 0;
-  for (; s0 + PF <= nst; s0 += PF) {
+  for (int i = 0; i < PF; ++i) {
+#pragma unroll
+    for (int r = 0; r < kStores; ++r) bstore4(0.0f, ro, kDropOffset + 4u * (4 * i + r));
+    load_next(i);
+  }
+  int q0 = 0;
+  for (; q0 + PF <= Q; q0 += PF) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      compute(i, s0 + i);
-      load(s0 + i + PF, i);
+      compute_next(i);
+      load_next(i);
     }
   }
 #pragma unroll
   for (int i = 0; i < PF; ++i)
-    if (s0 + i < nst) compute(i, s0 + i);
-
-  float sum[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const u32x2 sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
-    sum[r] = acc[r] + __uint_as_float(sw2.y);
-  }
-  finish_tile<N>(mt, chunk, tile, sum, mt.g);
+    if (q0 + i < Q) compute_next(i);
 }
 
 // ---- one FP8-row unit ------------------------------------------------------
@@ -405,14 +490,14 @@ __device__ void fp8_unit(const DevMat& mt, int chunk, int tile, const char* lds)
 // global unit list (matrix-major, then chunk, then tile).  For a single
 // matrix (mats == nullptr) the split is computed here, equal by units.
 template <int N, int MODE>
-__global__ __launch_bounds__(kThreads) void stream_kernel(const DevMat* __restrict__ mats,
+__global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const DevMat* __restrict__ mats,
                                                           const WgRange* __restrict__ ranges,
                                                           DevMat one) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   // wave-uniform values are pinned to scalar registers so that buffer
   // resources built from them stay uniform
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int nwaves = kWaves;
+  constexpr int nwaves = threads_for_mode<MODE>() / 64;
 
   int64_t u, u_end;
   int mi;
@@ -445,23 +530,31 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const DevMat* __restri
     __syncthreads();
     stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
     __syncthreads();
-    for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
-      const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
-      if constexpr (MODE == kModeNvfp4Aligned) {
-        nvfp4_unit<N, kPrefetch, true>(mt, chunk, tile, lds);
-      } else if constexpr (MODE == kModeNvfp4) {
-        nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
-      } else if constexpr (MODE == kModeFp8) {
-        fp8_unit<N, kPrefetch>(mt, chunk, tile, lds);
-      } else if constexpr (MODE == kModeNvfp4Tiled) {
-        nvfp4_tiled_unit<N, kPrefetchTiled>(mt, chunk, tile, lds);
+    // tiled NVFP4: wave w takes the w-th of nwaves equal shares of the run's
+    // consecutive tiles
+    const int64_t len = run_end - u;
+    const int64_t share0 = u + len * wave / nwaves, share1 = u + len * (wave + 1) / nwaves;
+    if constexpr (MODE == kModeNvfp4Tiled) {
+      nvfp4_tiled_run<N, kPrefetchTiled>(mt, chunk, share0, share1, lds);
+    } else {
+      if (MODE == kModeMixed && mt.fmt == kFmtNvfp4Tiled) {
+        nvfp4_tiled_run<N, 1>(mt, chunk, share0, share1, lds);
       } else {
-        if (mt.fmt == kFmtNvfp4)
-          nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
-        else if (mt.fmt == kFmtNvfp4Tiled)
-          nvfp4_tiled_unit<N, kPrefetchGeneric / 2>(mt, chunk, tile, lds);
-        else
-          fp8_unit<N, kPrefetchGeneric>(mt, chunk, tile, lds);
+        for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
+          const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
+          if constexpr (MODE == kModeNvfp4Aligned) {
+            nvfp4_unit<N, kPrefetch, true>(mt, chunk, tile, lds);
+          } else if constexpr (MODE == kModeNvfp4) {
+            nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
+          } else if constexpr (MODE == kModeFp8) {
+            fp8_unit<N, kPrefetch>(mt, chunk, tile, lds);
+          } else {
+            if (mt.fmt == kFmtNvfp4)
+              nvfp4_unit<N, kPrefetchGeneric, false>(mt, chunk, tile, lds);
+            else
+              fp8_unit<N, kPrefetchGeneric>(mt, chunk, tile, lds);
+          }
+        }
       }
     }
     u = run_end;
@@ -515,7 +608,8 @@ static hipError_t launch_nm(const DevMat* mats, const WgRange* ranges, const Dev
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((stream_kernel<N, MODE>), dim3(grid), dim3(kThreads), lds_bytes, stream, mats, ranges, one);
+  hipLaunchKernelGGL((stream_kernel<N, MODE>), dim3(grid), dim3(threads_for_mode<MODE>()), lds_bytes, stream, mats,
+                     ranges, one);
   return hipGetLastError();
 }
 

@@ -98,3 +98,30 @@ def test_tiled_verify_pass_dense_layer(wq, N):
         rows = np.unique(np.concatenate([rng.integers(0, m.M, 500), [0, m.M - 1]]))
         yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x, rows=rows)
         assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "tiled pass M=%d K=%d N=%d" % (m.M, m.K, N))
+
+
+def test_tiled_verify_pass_column_invariance(wq):
+    # Long rows are staged in one K chunk when the N columns fit in LDS
+    # (N <= 4 here) and in two otherwise; both must give the same bits,
+    # including a ragged last summation chunk (K = 17440).
+    specs = [(96, 17408), (40, 17440), (33, 8736), (17, 544)]
+    host = [inputs.nvfp4_inputs(M, K, 8, seed=1200 + i, g=0.02) for i, (M, K) in enumerate(specs)]
+    tiled = [to_tiled(wq, d) for d in host]
+    xs = [dev_bf16bits(d.x) for d in host]
+    outs = {}
+    for N in range(1, 9):
+        mats = []
+        for d, t, x in zip(host, tiled, xs):
+            y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
+            mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, t, None, x[:N].contiguous(), y, d.g))
+        ws = workspace(wq.wq_verify_workspace_bytes(mats, N))
+        print("column invariance N=%d workspace=%d" % (N, 0 if ws is None else ws.numel()), flush=True)
+        wq.wq_verify_pass(mats, N, ws)
+        torch.cuda.synchronize()
+        outs[N] = [m.y.cpu().numpy() for m in mats]
+    for i, d in enumerate(host):
+        yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x)
+        assert_close(outs[8][i], yr, ar, "pass M=%d K=%d N=8" % (d.M, d.K))
+        for N in range(1, 8):
+            assert np.array_equal(outs[N][i].view(np.uint32), outs[8][i][:N].view(np.uint32)), \
+                "M=%d K=%d: N=%d differs from N=8" % (d.M, d.K, N)
