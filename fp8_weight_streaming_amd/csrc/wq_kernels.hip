@@ -84,12 +84,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* 
                                            kRsrcWord3);
 }
 
-// Output stores of the tiled stream are written through to memory (system
-// scope: sc0 sc1).  With the weight loads non-temporal, write-back made the
-// dirty output lines leave the L2 later as evictions that cost the read
-// stream more (measured on MI355X: 5.7-6.1 TB/s write-back against
-// 5.9-6.3 TB/s write-through over the dense 64-layer pass).
-constexpr int kAuxOut = 17;
+// Output stores of the tiled stream are written through the L2 (device
+// scope, sc1).  With the weight loads non-temporal, the default write-back
+// policy left dirty output lines to leave the L2 later as evictions, which
+// cost the read stream more: over the dense 64-layer pass on MI355X, paired
+// full-line stores ran at 6.17 / 5.93 / 5.74 TB/s (N = 2 / 4 / 8) written
+// back and 6.44 / 6.33 / 6.07 TB/s written through; system scope measured
+// the same as device scope, and the non-temporal hint was slower.
+constexpr int kAuxOut = 16;
 __device__ __forceinline__ void bstore4(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kAuxOut);
 }
@@ -359,7 +361,12 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
       for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(stv[t], part[t][r], acc[r]);
   };
   // Outputs: y (scaled by g) for an unsplit matrix, else this chunk's plane
-  // of the partial sums; lanes 0..31 hold n = nb + r, m = 16 * tile + c.
+  // of the partial sums, both [N][M].  Tiles are written in pairs (global
+  // tiles 2j and 2j + 1, consecutive in the wave's share): a tile's sums wait
+  // in registers for the next tile's, and then each store instruction writes
+  // two whole 128-byte lines, rows n and n + 4 of 32 consecutive m.  A tile
+  // without its partner in the share is written alone, as half lines.
+  //
   // Every step issues the same min(N, 4) stores; only on a tile's last step
   // do their offsets point into the buffer, otherwise the range check drops
   // them.  An equal count of memory operations on every step keeps the
@@ -370,8 +377,8 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
   float* const obase = split ? mt.part + (size_t)chunk * N * mt.M : mt.y;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc_uniform(obase, (uint64_t)N * (uint64_t)mt.M * 4u);
   const float oscale = split ? 1.0f : mt.g;
-  const int nb = 4 * (lane >> 4);
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  float prev[4] = {0.f, 0.f, 0.f, 0.f};
   uint32_t so[4] = {kDropOffset, kDropOffset, kDropOffset, kDropOffset};
 
   // next step to compute: tile ci, step cst
@@ -382,15 +389,32 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
     half(c1[slot], sw[slot].y, xo + 256u * N);
     const bool fin = cst == nst - 1;
     if (fin) {
-      // lanes l and l+32 hold blocks 0 and 1 of the same (n, m): add in that order
-      const int m = (tile0 + ci) * 16 + c;
+      const int t = tile0 + ci;
+      const bool odd = (t & 1) != 0;
+      // emit a pair (odd tile), or a lone even tile at the end of the share
+      const bool emit = odd || ci == cnt - 1;
+      // store lanes: n = r + 4 * (lane / 32), m = m0 + lane % 32, where
+      // m % 32 < 16 comes from the even tile and the rest from the odd one
+      const int m = 16 * (odd ? t - 1 : t) + (lane & 31);
+      const bool half_ok = (lane & 16) ? odd : (!odd || ci > 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        // lanes l and l+32 hold blocks 0 and 1 of the same (n, m): the swap
+        // gives every lane both (.x the low half's, .y the high half's), and
+        // they are added in that order, so both lanes hold the same sum
         const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
-        sum[r] = oscale * (acc[r] + __uint_as_float(p.y));
+        const float cur = oscale * (__uint_as_float(p.x) + __uint_as_float(p.y));
         acc[r] = 0.f;
-        const bool live = lane < 32 && m < mt.M && nb + r < N;
-        so[r] = live ? (uint32_t)(((nb + r) * mt.M + m) * 4) : kDropOffset;
+        // sums sit at lane 16 * (n / 4) + m % 16 (and again 32 lanes up):
+        // the 16-lane swap brings the even tile to rows 0 and 2 and the odd
+        // tile to rows 1 and 3
+        const u32x2 q = __builtin_amdgcn_permlane16_swap(__float_as_uint(odd ? prev[r] : cur), __float_as_uint(cur),
+                                                         false, false);
+        sum[r] = __uint_as_float(lane < 32 ? q.x : q.y);
+        prev[r] = cur;
+        const int n = r + 4 * (lane >> 5);
+        const bool live = emit && half_ok && m < mt.M && n < N;
+        so[r] = live ? (uint32_t)((n * mt.M + m) * 4) : kDropOffset;
       }
     }
 #pragma unroll
