@@ -83,8 +83,10 @@ Split verify_split(int fmt, int M, int K) {
 // A single product may split K further so that every wave of every CU has
 // a unit of work.  Candidate splits are scored by the work of the busiest
 // wave: rounds of units times (segments per unit + a ramp of kPrefetch
-// segments); a split must save at least 10% over the next-coarser best to
-// be taken, since it costs partial-sum traffic.
+// segments), plus, for any split, the reduce launch (about 4 us on MI355X,
+// taken as 6 tiled steps or 12 segments of the other formats); a split must
+// save at least 10% over the next-coarser best to be taken, since it also
+// costs partial-sum traffic.
 Split gemm_split(int fmt, int M, int K, int cus) {
   const int sk = seg_k(fmt);
   const int64_t slots = (int64_t)cus * waves_for_mode(fmt == kFmtNvfp4Tiled ? kModeNvfp4Tiled : kModeNvfp4);
@@ -99,7 +101,8 @@ Split gemm_split(int fmt, int M, int K, int cus) {
     if (nc != n && n != nmin) continue;  // this n rounds to a split already scored
     const int64_t units = ntiles * nc;
     const int64_t rounds = ceil_div(units, slots);
-    const double cost = (double)rounds * ((double)(kc / sk) + kPrefetch);
+    const double reduce_cost = nc > 1 ? (fmt == kFmtNvfp4Tiled ? 6.0 : 12.0) : 0.0;
+    const double cost = (double)rounds * ((double)(kc / sk) + kPrefetch) + reduce_cost;
     if (cost < 0.9 * best_cost) {
       best_cost = cost;
       best = make_split(fmt, M, K, kc);

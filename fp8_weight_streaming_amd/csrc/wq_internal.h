@@ -81,7 +81,9 @@ struct ReduceTask {
   int32_t count;  // outputs in the run (<= kReduceRun)
 };
 constexpr int kReduceThreads = 256;
-constexpr int kReduceRun = 4096;
+// One output per thread: a split product can have few outputs (40,960 for
+// 5120 rows at N = 8), and the sum over chunks is one round of loads.
+constexpr int kReduceRun = kReduceThreads;
 
 // Kernel variants: which unit bodies a launch contains.
 constexpr int kModeNvfp4Aligned = 0;  // NVFP4 only, K % 64 == 0 for every matrix

@@ -134,14 +134,17 @@ __device__ __forceinline__ bf16x8 lds_read16(const char* lds, uint32_t off) {
 // ---- staging of one K chunk of X into LDS --------------------------------
 // LDS layout: piece (kc, n) = X[n][k0 + 8kc .. k0 + 8kc + 7] (16 bytes) at
 // byte (kc * N + n) * 16, for kc < kc_pad (pieces past the chunk are zero).
+constexpr int kStageLoads = 8;
 template <int N>
 __device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0, int klen, int kc_pad) {
   const int valid = klen / 8;
   const int total = kc_pad * N;
-  for (int p0 = threadIdx.x; p0 < total; p0 += 4 * (int)blockDim.x) {
-    u32x4 v[4];
+  // eight 16-byte loads in flight per thread before any LDS store: staging
+  // is a few rounds of L2/HBM latency, and at the start of every run
+  for (int p0 = threadIdx.x; p0 < total; p0 += kStageLoads * (int)blockDim.x) {
+    u32x4 v[kStageLoads];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kStageLoads; ++j) {
       const int p = p0 + j * (int)blockDim.x;
       const int n = p / kc_pad, kc = p - n * kc_pad;
       v[j] = u32x4{0u, 0u, 0u, 0u};
@@ -149,7 +152,7 @@ __device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0
         v[j] = *reinterpret_cast<const u32x4*>(x + (size_t)n * K + k0 + 8 * kc);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kStageLoads; ++j) {
       const int p = p0 + j * (int)blockDim.x;
       const int n = p / kc_pad, kc = p - n * kc_pad;
       if (p < total) *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = v[j];
@@ -608,6 +611,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const DevMat* __
     const int64_t o = t.begin + i;  // = n * M + m
     const int m = (int)(o % mt.M);
     float acc = 0.0f;
+#pragma unroll 8
     for (int c = 0; c < mt.nchunks; ++c) acc += mt.part[c * plane + o];
     // row scales exist only for FP8-row; both NVFP4 layouts use g
     const float scale = mt.fmt == kFmtFp8Row ? mt.rs[m] : mt.g;
