@@ -60,8 +60,12 @@ struct Split {
   int ntiles = 0;
 };
 
-int seg_k(int fmt) { return fmt == kFmtNvfp4Tiled ? kTileStepK : fmt == kFmtNvfp4 ? 128 : 64; }
+int seg_k(int fmt) {
+  return fmt == kFmtNvfp4Tiled ? kTileStepK : fmt == kFmtFp8RowTiled ? kFp8TileStepK : fmt == kFmtNvfp4 ? 128 : 64;
+}
 bool is_nvfp4(int fmt) { return fmt == kFmtNvfp4 || fmt == kFmtNvfp4Tiled; }
+bool is_fp8(int fmt) { return fmt == kFmtFp8Row || fmt == kFmtFp8RowTiled; }
+bool is_tiled(int fmt) { return fmt == kFmtNvfp4Tiled || fmt == kFmtFp8RowTiled; }
 
 Split make_split(int fmt, int M, int K, int kc) {
   Split s;
@@ -89,7 +93,7 @@ Split verify_split(int fmt, int M, int K) {
 // costs partial-sum traffic.
 Split gemm_split(int fmt, int M, int K, int cus) {
   const int sk = seg_k(fmt);
-  const int64_t slots = (int64_t)cus * waves_for_mode(fmt == kFmtNvfp4Tiled ? kModeNvfp4Tiled : kModeNvfp4);
+  const int64_t slots = (int64_t)cus * waves_for_mode(is_tiled(fmt) ? kModeTiled : kModeNvfp4);
   const int64_t ntiles = ceil_div(M, 16);
   const int nmin = (int)ceil_div(K, kKcMax);
   const int nmax = std::max(nmin, (int)std::min<int64_t>(64, ceil_div(K, sk)));
@@ -101,7 +105,7 @@ Split gemm_split(int fmt, int M, int K, int cus) {
     if (nc != n && n != nmin) continue;  // this n rounds to a split already scored
     const int64_t units = ntiles * nc;
     const int64_t rounds = ceil_div(units, slots);
-    const double reduce_cost = nc > 1 ? (fmt == kFmtNvfp4Tiled ? 6.0 : 12.0) : 0.0;
+    const double reduce_cost = nc > 1 ? (is_tiled(fmt) ? 6.0 : 12.0) : 0.0;
     const double cost = (double)rounds * ((double)(kc / sk) + kPrefetch) + reduce_cost;
     if (cost < 0.9 * best_cost) {
       best_cost = cost;
@@ -113,7 +117,8 @@ Split gemm_split(int fmt, int M, int K, int cus) {
 
 // ---- validation ------------------------------------------------------------------
 wq_status check_shape(int fmt, int M, int K, int N) {
-  if (fmt != kFmtNvfp4 && fmt != kFmtFp8Row && fmt != kFmtNvfp4Tiled) return WQ_ERROR_INVALID_VALUE;
+  if (fmt != kFmtNvfp4 && fmt != kFmtFp8Row && fmt != kFmtNvfp4Tiled && fmt != kFmtFp8RowTiled)
+    return WQ_ERROR_INVALID_VALUE;
   if (N < 1 || N > 8 || M < 1 || K < 1) return WQ_ERROR_INVALID_VALUE;
   const int mult = is_nvfp4(fmt) ? 32 : 16;
   if (K % mult != 0 || K > (1 << 24)) return WQ_ERROR_UNSUPPORTED_SHAPE;
@@ -124,6 +129,10 @@ wq_status check_shape(int fmt, int M, int K, int N) {
   // a tiled matrix is addressed with 32-bit buffer offsets
   if (fmt == kFmtNvfp4Tiled &&
       (uint64_t)((M + kTileRows - 1) / kTileRows) * ((K + kTileStepK - 1) / kTileStepK) * kTileBlockBytes >= (1ull << 32))
+    return WQ_ERROR_UNSUPPORTED_SHAPE;
+  if (fmt == kFmtFp8RowTiled &&
+      (uint64_t)((M + kTileRows - 1) / kTileRows) * ((K + kFp8TileStepK - 1) / kFp8TileStepK) * kFp8TileBlockBytes >=
+          (1ull << 32))
     return WQ_ERROR_UNSUPPORTED_SHAPE;
   return WQ_SUCCESS;
 }
@@ -146,8 +155,8 @@ DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x
                const Split& sp, char* scratch, int N, int64_t unit0) {
   DevMat d{};
   d.w = static_cast<const uint8_t*>(w);
-  d.s = fmt == kFmtNvfp4 ? static_cast<const uint8_t*>(s) : nullptr;  // tiled: inside w
-  d.rs = fmt == kFmtFp8Row ? static_cast<const float*>(s) : nullptr;
+  d.s = fmt == kFmtNvfp4 ? static_cast<const uint8_t*>(s) : nullptr;  // tiled NVFP4: inside w
+  d.rs = is_fp8(fmt) ? static_cast<const float*>(s) : nullptr;
   d.x = x;
   d.y = y;
   d.g = g;
@@ -178,7 +187,7 @@ wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x
   const int64_t units = (int64_t)sp.nchunks * sp.ntiles;
   const int grid = (int)std::min<int64_t>(cus, units);
   const int mode = fmt == kFmtFp8Row ? kModeFp8
-                   : fmt == kFmtNvfp4Tiled ? kModeNvfp4Tiled
+                   : is_tiled(fmt) ? kModeTiled
                    : (K % 64 == 0 ? kModeNvfp4Aligned : kModeNvfp4);
   hipError_t e = launch_stream(N, mode, nullptr, nullptr, one, grid, lds_bytes_for(N),
                                static_cast<hipStream_t>(stream));
@@ -336,6 +345,11 @@ wq_status wq_gemm_fp8row(const uint8_t* w, const float* row_scale, const uint16_
   return gemm(kFmtFp8Row, w, row_scale, 1.0f, x, y, M, K, N, workspace, workspace_bytes, stream);
 }
 
+wq_status wq_gemm_fp8row_tiled(const uint8_t* tiled, const float* row_scale, const uint16_t* x, float* y, int M,
+                               int K, int N, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm(kFmtFp8RowTiled, tiled, row_scale, 1.0f, x, y, M, K, N, workspace, workspace_bytes, stream);
+}
+
 size_t wq_verify_workspace_bytes(const wq_matrix* descs, int count, int N) {
   if (check_descs(descs, count, N) != WQ_SUCCESS) return 0;
   const int cus = current_cus();
@@ -372,7 +386,7 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
     if (d.fmt == kFmtNvfp4) {
       any_nv = true;
       all_aligned = all_aligned && d.K % 64 == 0;
-    } else if (d.fmt == kFmtNvfp4Tiled) {
+    } else if (is_tiled(d.fmt)) {
       any_tiled = true;
     } else {
       any_fp8 = true;
@@ -393,7 +407,7 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
   const int kinds = (int)any_nv + (int)any_fp8 + (int)any_tiled;
   plan->mode = kinds > 1 ? kModeMixed
                : any_fp8 ? kModeFp8
-               : any_tiled ? kModeNvfp4Tiled
+               : any_tiled ? kModeTiled
                : all_aligned ? kModeNvfp4Aligned : kModeNvfp4;
   plan->grid = L.grid;
   plan->ranges_offset = L.table_bytes;
@@ -404,7 +418,7 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
 
 wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {
   if (!plan || !plan->workspace || plan->N < 1 || plan->N > 8 || plan->grid < 1 || plan->count < 1 ||
-      plan->mode < kModeNvfp4Aligned || plan->mode > kModeNvfp4Tiled || plan->ranges_offset >= plan->workspace_bytes ||
+      plan->mode < kModeNvfp4Aligned || plan->mode > kModeTiled || plan->ranges_offset >= plan->workspace_bytes ||
       plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes))
     return WQ_ERROR_INVALID_VALUE;
   const char* ws = static_cast<const char*>(plan->workspace);

@@ -11,6 +11,7 @@ namespace wq {
 constexpr int kFmtNvfp4 = 0;
 constexpr int kFmtFp8Row = 1;
 constexpr int kFmtNvfp4Tiled = 2;
+constexpr int kFmtFp8RowTiled = 3;
 
 // Tiled NVFP4 storage: blocks of 16 rows x 256 k, each 2048 bytes of codes
 // (two 1 KB halves in MFMA lane order) followed by 256 bytes of block
@@ -19,6 +20,10 @@ constexpr int kTileRows = 16;
 constexpr int kTileStepK = 256;
 constexpr int kTileCodeBytes = 2048;
 constexpr int kTileBlockBytes = 2304;
+// Tiled FP8-row storage: blocks of 16 rows x 128 k (2048 bytes, two 1 KB
+// halves of 16 row bytes per MFMA lane).
+constexpr int kFp8TileStepK = 128;
+constexpr int kFp8TileBlockBytes = 2048;
 
 // One persistent workgroup per CU: 16 waves of 64 lanes (8 waves with twice
 // the registers each for the tiled-NVFP4 kernel, whose ring spans tiles).
@@ -53,7 +58,7 @@ static_assert(kMaxLdsBytes <= 160u * 1024u, "LDS budget exceeded");
 
 // Device-side descriptor of one matrix (built on the host).
 struct DevMat {
-  const uint8_t* w;   // NVFP4 codes [M][K/2], FP8 codes [M][K] or tiled NVFP4 blocks
+  const uint8_t* w;   // NVFP4 codes [M][K/2], FP8 codes [M][K], or tiled NVFP4 / FP8 blocks
   const uint8_t* s;   // NVFP4 block scales [M][K/16] (null for FP8-row)
   const float* rs;    // FP8 row scales [M] (null for NVFP4)
   const uint16_t* x;  // BF16 [N][K]
@@ -90,11 +95,11 @@ constexpr int kModeNvfp4Aligned = 0;  // NVFP4 only, K % 64 == 0 for every matri
 constexpr int kModeNvfp4 = 1;         // NVFP4 only, any K % 32 == 0
 constexpr int kModeFp8 = 2;           // FP8-row only
 constexpr int kModeMixed = 3;         // any formats
-constexpr int kModeNvfp4Tiled = 4;    // tiled NVFP4 only
+constexpr int kModeTiled = 4;         // tiled NVFP4 and tiled FP8-row only
 
 template <int MODE>
-__host__ __device__ constexpr int threads_for_mode() { return MODE == kModeNvfp4Tiled ? kThreadsTiled : kThreads; }
-constexpr int waves_for_mode(int mode) { return (mode == kModeNvfp4Tiled ? kThreadsTiled : kThreads) / 64; }
+__host__ __device__ constexpr int threads_for_mode() { return MODE == kModeTiled ? kThreadsTiled : kThreads; }
+constexpr int waves_for_mode(int mode) { return (mode == kModeTiled ? kThreadsTiled : kThreads) / 64; }
 
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);

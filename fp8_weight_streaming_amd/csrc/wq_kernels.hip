@@ -295,43 +295,64 @@ __device__ void nvfp4_unit(const DevMat& mt, int chunk, int tile, const char* ld
   finish_tile<N>(mt, chunk, tile, sum, mt.g);
 }
 
-// ---- a wave's tiled-NVFP4 tiles of one run ----------------------------------
-// Same arithmetic as nvfp4_unit, on weights stored by wq_nvfp4_tile: a step
-// of 256 k is one 2304-byte block per 16-row tile, so each lane's loads are
-// 16 bytes of one contiguous 1 KB (codes, twice) plus 8 bytes of one
-// contiguous 256 B (scales), with the codes already in the order the MFMA
-// B operand wants and the scales already split by parity.
+// ---- a wave's tiles of one run, tiled NVFP4 or tiled FP8-row ----------------
+// NVFP4 (FP8 = false): the arithmetic of nvfp4_unit, on weights stored by
+// wq_nvfp4_tile.  A step of 256 k is one 2304-byte block per 16-row tile, so
+// each lane's loads are 16 bytes of one contiguous 1 KB (codes, twice) plus
+// 8 bytes of one contiguous 256 B (scales), with the codes already in the
+// order the MFMA B operand wants and the scales already split by parity.
+//
+// FP8-row (FP8 = true): the arithmetic of fp8_unit, on weights stored by
+// wq_fp8_tile.  A step of 128 k is one 2048-byte block per tile; each of a
+// lane's two 16-byte loads is the 16 row bytes fp8_unit gathers for one
+// 64-k segment, so the MFMA sequence (and the result) is fp8_unit's.  The
+// row scale of the lane's row comes with every step (a 4-byte load that
+// hits the cache), so that every step issues the same memory operations.
 //
 // The wave takes the consecutive tiles [first, end) of one matrix and K
 // chunk (all nst steps long).  They lie back to back in memory, so the
 // wave's whole share is one sequential stream, and it is streamed as ONE
 // sequence of steps: the ring keeps PF steps in flight across tile
 // boundaries.
-
-template <int N, int PF>
-__device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds) {
+template <int N, int PF, bool FP8>
+__device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds) {
   if (first >= end) return;
+  constexpr int kStep = FP8 ? kFp8TileStepK : kTileStepK;
+  constexpr uint32_t kBlock = FP8 ? kFp8TileBlockBytes : kTileBlockBytes;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const int k0 = chunk * mt.kc;
   const int klen = min(mt.kc, mt.K - k0);
-  const int nst = (klen + kTileStepK - 1) / kTileStepK;
+  const int nst = (klen + kStep - 1) / kStep;
   const int cnt = (int)(end - first);
   const int tile0 = (int)((first - mt.unit0) - (int64_t)chunk * mt.ntiles);
-  const uint32_t steps_per_row = (uint32_t)((mt.K + kTileStepK - 1) / kTileStepK);
-  const uint32_t base_step = (uint32_t)(k0 / kTileStepK);
-  const uint64_t total = (uint64_t)mt.ntiles * steps_per_row * kTileBlockBytes;  // < 2^32 (checked on the host)
+  const uint32_t steps_per_row = (uint32_t)((mt.K + kStep - 1) / kStep);
+  const uint32_t base_step = (uint32_t)(k0 / kStep);
+  const uint64_t total = (uint64_t)mt.ntiles * steps_per_row * kBlock;  // < 2^32 (checked on the host)
   const __amdgpu_buffer_rsrc_t rw = make_rsrc_uniform(mt.w, total);
   const uint32_t vc = 16u * lane;
   const uint32_t vs = (uint32_t)kTileCodeBytes + 8u * (uint32_t)(((lane >> 5) << 4) + c);
+  // FP8 row scales: rows past M read as 0 (range check)
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc_uniform(mt.rs, FP8 ? (uint64_t)mt.M * 4u : 0u);
 
-  const bool active = ((c >> 3) == (g >> 1)) && ((c & 7) < N);
-  const uint32_t xoff = active ? (uint32_t)((g * N + (c & 7)) * 16) : kZeroOffset<N>();
-  const uint32_t xstep = active ? 512u * N : 0u;
+  // A operand (X) in LDS.  NVFP4: rows (scale block b, column n), so a lane
+  // is live where its k slots belong to its block; FP8: rows are columns.
+  bool active;
+  uint32_t xoff, xstep;
+  if constexpr (FP8) {
+    active = c < N;
+    xoff = active ? (uint32_t)((2 * g * N + c) * 16) : kZeroOffset<N>();
+    xstep = active ? 256u * N : 0u;
+  } else {
+    active = ((c >> 3) == (g >> 1)) && ((c & 7) < N);
+    xoff = active ? (uint32_t)((g * N + (c & 7)) * 16) : kZeroOffset<N>();
+    xstep = active ? 512u * N : 0u;
+  }
 
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   u32x4 c0[PF], c1[PF];
-  u32x2 sw[PF];
+  u32x2 sw[PF];     // NVFP4 block scales
+  uint32_t rv[PF];  // FP8 row scale bits
 
   // next step to load: tile li, step lst (past the end: the last step again)
   int li = 0, lst = 0;
@@ -339,12 +360,16 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
     const bool past = li >= cnt;
     const uint32_t ti = (uint32_t)(past ? cnt - 1 : li);
     const uint32_t ts = (uint32_t)(past ? nst - 1 : lst);
-    const uint32_t b = (((uint32_t)tile0 + ti) * steps_per_row + base_step + ts) * kTileBlockBytes;
+    const uint32_t b = (((uint32_t)tile0 + ti) * steps_per_row + base_step + ts) * kBlock;
     c0[slot] = bload16t(rw, b + vc);
     c1[slot] = bload16t(rw, b + 1024u + vc);
-    sw[slot] = bload8t(rw, b + vs);
+    if constexpr (FP8)
+      rv[slot] = __builtin_amdgcn_raw_buffer_load_b32(rr, (int)(((tile0 + ti) * 16u + c) * 4u), 0, 0);
+    else
+      sw[slot] = bload8t(rw, b + vs);
     if (++lst == nst) { lst = 0; ++li; }
   };
+  // NVFP4: half a step (128 k) of one slot
   auto half = [&](const u32x4& e, uint32_t sb, uint32_t xo) {
     const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
     const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, true);
@@ -363,6 +388,16 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(stv[t], part[t][r], acc[r]);
   };
+  // FP8: one 64-k segment (16 bytes of the lane's row)
+  auto segment = [&](const u32x4& d, uint32_t xo) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) a[u] = lds_read16(lds, xo + u * 16u * N);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) b[u] = e4m3x8_to_bf16(d[2 * u], d[2 * u + 1]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+  };
   // Outputs: y (scaled by g) for an unsplit matrix, else this chunk's plane
   // of the partial sums, both [N][M].  Tiles are written in pairs (global
   // tiles 2j and 2j + 1, consecutive in the wave's share): a tile's sums wait
@@ -379,7 +414,7 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
   const bool split = mt.nchunks > 1;
   float* const obase = split ? mt.part + (size_t)chunk * N * mt.M : mt.y;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc_uniform(obase, (uint64_t)N * (uint64_t)mt.M * 4u);
-  const float oscale = split ? 1.0f : mt.g;
+  const float gscale = split ? 1.0f : mt.g;
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
   float prev[4] = {0.f, 0.f, 0.f, 0.f};
   uint32_t so[4] = {kDropOffset, kDropOffset, kDropOffset, kDropOffset};
@@ -388,8 +423,13 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
   int ci = 0, cst = 0;
   auto compute_next = [&](int slot) {
     const uint32_t xo = xoff + (uint32_t)cst * xstep;
-    half(c0[slot], sw[slot].x, xo);
-    half(c1[slot], sw[slot].y, xo + 256u * N);
+    if constexpr (FP8) {
+      segment(c0[slot], xo);
+      segment(c1[slot], xo + 128u * N);
+    } else {
+      half(c0[slot], sw[slot].x, xo);
+      half(c1[slot], sw[slot].y, xo + 256u * N);
+    }
     const bool fin = cst == nst - 1;
     if (fin) {
       const int t = tile0 + ci;
@@ -400,13 +440,18 @@ __device__ void nvfp4_tiled_run(const DevMat& mt, int chunk, int64_t first, int6
       // m % 32 < 16 comes from the even tile and the rest from the odd one
       const int m = 16 * (odd ? t - 1 : t) + (lane & 31);
       const bool half_ok = (lane & 16) ? odd : (!odd || ci > 0);
+      // the FP8 row scale of the lane's row (m = 16 t + c); 1 for partials
+      const float rscale = split ? 1.0f : __uint_as_float(rv[slot]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // lanes l and l+32 hold blocks 0 and 1 of the same (n, m): the swap
-        // gives every lane both (.x the low half's, .y the high half's), and
-        // they are added in that order, so both lanes hold the same sum
+        // the swap gives every lane the low half's value (.x) and the high
+        // half's (.y).  NVFP4: lanes l and l+32 hold blocks 0 and 1 of the
+        // same (n, m); they are added in that order, so both lanes hold the
+        // same sum.  FP8: lanes 0..31 hold rows n < 8 (the upper half holds
+        // rows 8..15, which are zero), copied to both halves.
         const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
-        const float cur = oscale * (__uint_as_float(p.x) + __uint_as_float(p.y));
+        const float cur = FP8 ? rscale * __uint_as_float(p.x)
+                              : gscale * (__uint_as_float(p.x) + __uint_as_float(p.y));
         acc[r] = 0.f;
         // sums sit at lane 16 * (n / 4) + m % 16 (and again 32 lanes up):
         // the 16-lane swap brings the even tile to rows 0 and 2 and the odd
@@ -552,7 +597,12 @@ __global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const 
     const int64_t run_end = min(u_end, mt.unit0 + (int64_t)(chunk + 1) * mt.ntiles);
     const int k0 = chunk * mt.kc;
     const int klen = min(mt.kc, mt.K - k0);
-    const int seg_k = mt.fmt == kFmtNvfp4Tiled ? kTileStepK : mt.fmt == kFmtNvfp4 ? 128 : 64;
+    // X is staged (zero-padded) to whole steps of the format, which every
+    // lane of the last step reads
+    const int seg_k = mt.fmt == kFmtNvfp4Tiled    ? kTileStepK
+                      : mt.fmt == kFmtFp8RowTiled ? kFp8TileStepK
+                      : mt.fmt == kFmtNvfp4       ? 128
+                                                  : 64;
     const int kc_pad = ((klen + seg_k - 1) / seg_k) * (seg_k / 8);
     __syncthreads();
     stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
@@ -561,11 +611,16 @@ __global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const 
     // consecutive tiles
     const int64_t len = run_end - u;
     const int64_t share0 = u + len * wave / nwaves, share1 = u + len * (wave + 1) / nwaves;
-    if constexpr (MODE == kModeNvfp4Tiled) {
-      nvfp4_tiled_run<N, kPrefetchTiled>(mt, chunk, share0, share1, lds);
+    if constexpr (MODE == kModeTiled) {
+      if (mt.fmt == kFmtFp8RowTiled)
+        tiled_run<N, kPrefetchTiled, true>(mt, chunk, share0, share1, lds);
+      else
+        tiled_run<N, kPrefetchTiled, false>(mt, chunk, share0, share1, lds);
     } else {
       if (MODE == kModeMixed && mt.fmt == kFmtNvfp4Tiled) {
-        nvfp4_tiled_run<N, 1>(mt, chunk, share0, share1, lds);
+        tiled_run<N, 1, false>(mt, chunk, share0, share1, lds);
+      } else if (MODE == kModeMixed && mt.fmt == kFmtFp8RowTiled) {
+        tiled_run<N, 1, true>(mt, chunk, share0, share1, lds);
       } else {
         for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
           const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
@@ -614,7 +669,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const DevMat* __
 #pragma unroll 8
     for (int c = 0; c < mt.nchunks; ++c) acc += mt.part[c * plane + o];
     // row scales exist only for FP8-row; both NVFP4 layouts use g
-    const float scale = mt.fmt == kFmtFp8Row ? mt.rs[m] : mt.g;
+    const float scale = (mt.fmt == kFmtFp8Row || mt.fmt == kFmtFp8RowTiled) ? mt.rs[m] : mt.g;
     mt.y[o] = scale * acc;
   }
 }
@@ -649,7 +704,7 @@ static hipError_t launch_n(int mode, const DevMat* mats, const WgRange* ranges, 
     case kModeNvfp4: return launch_nm<N, kModeNvfp4>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeFp8: return launch_nm<N, kModeFp8>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeMixed: return launch_nm<N, kModeMixed>(mats, ranges, one, grid, lds_bytes, stream);
-    case kModeNvfp4Tiled: return launch_nm<N, kModeNvfp4Tiled>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeTiled: return launch_nm<N, kModeTiled>(mats, ranges, one, grid, lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

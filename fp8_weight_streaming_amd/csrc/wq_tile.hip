@@ -1,5 +1,6 @@
-// wq_tile.hip -- conversion between the plain NVFP4 layout and the tiled
-// layout that wq's NVFP4 kernels stream fastest (a load-time, untimed step).
+// wq_tile.hip -- conversion between the plain NVFP4 / FP8-row layouts and
+// the tiled layouts that wq's kernels stream fastest (a load-time, untimed
+// step).
 //
 // The crit-hub engine card "mtp7-device-confidence" (section "Design", row
 // "Weights") keeps its NVFP4 scales in a swizzled tile order chosen for its
@@ -15,6 +16,13 @@
 //     row 16t + c (eight E2M1 codes, low nibble first);
 //   bytes [2048 + 8(16p + c) + 4h + j], p = 0..1: the E4M3 scale of row
 //     16t + c for block 16s + 8h + 2j + p.
+//
+// Tiled FP8-row layout, for T = ceil(M/16) row tiles and S = ceil(K/128)
+// steps: block (t, s), at byte (t*S + s)*2048, holds rows 16t..16t+15 and
+// k = 128s .. 128s+127 (rows >= M and k >= K read as zero bytes):
+//   bytes [1024h + 16l, +16), h = 0..1, lane l = c + 16g: plain bytes
+//     [128s + 64h + 16g, +16) of row 16t + c.
+// The row scales stay a separate FP32 array.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -100,6 +108,54 @@ __global__ __launch_bounds__(kTileThreads) void untile_kernel(const uint8_t* __r
   }
 }
 
+// One thread per (tile, step, lane): two 16-byte pieces of one row.
+__global__ __launch_bounds__(kTileThreads) void fp8_tile_kernel(const uint8_t* __restrict__ w, int M, int K,
+                                                                uint8_t* __restrict__ tiled, int64_t slots) {
+  const int64_t id = (int64_t)blockIdx.x * kTileThreads + threadIdx.x;
+  if (id >= slots) return;
+  const int S = (K + kFp8TileStepK - 1) / kFp8TileStepK;
+  const int l = (int)(id & 63);
+  const int64_t ts = id >> 6;
+  const int s = (int)(ts % S);
+  const int64_t t = ts / S;
+  const int c = l & 15, g = l >> 4;
+  const int64_t row = t * kTileRows + c;
+  uint8_t* blk = tiled + ts * kFp8TileBlockBytes;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = (int64_t)kFp8TileStepK * s + 64 * h + 16 * g;  // K % 16 == 0: a piece is all in or all out
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < M && k < K) v = *reinterpret_cast<const uint4*>(w + row * K + k);
+    *reinterpret_cast<uint4*>(blk + 1024 * h + 16 * l) = v;
+  }
+}
+
+__global__ __launch_bounds__(kTileThreads) void fp8_untile_kernel(const uint8_t* __restrict__ tiled, int M, int K,
+                                                                  uint8_t* __restrict__ w, int64_t slots) {
+  const int64_t id = (int64_t)blockIdx.x * kTileThreads + threadIdx.x;
+  if (id >= slots) return;
+  const int S = (K + kFp8TileStepK - 1) / kFp8TileStepK;
+  const int l = (int)(id & 63);
+  const int64_t ts = id >> 6;
+  const int s = (int)(ts % S);
+  const int64_t t = ts / S;
+  const int c = l & 15, g = l >> 4;
+  const int64_t row = t * kTileRows + c;
+  if (row >= M) return;
+  const uint8_t* blk = tiled + ts * kFp8TileBlockBytes;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = (int64_t)kFp8TileStepK * s + 64 * h + 16 * g;
+    if (k < K) *reinterpret_cast<uint4*>(w + row * K + k) = *reinterpret_cast<const uint4*>(blk + 1024 * h + 16 * l);
+  }
+}
+
+bool fp8_shape_ok(int M, int K) {
+  return M >= 1 && K >= 16 && K % 16 == 0 && K <= (1 << 24) && (uint64_t)M * (uint64_t)K < (1ull << 40);
+}
+
+int64_t fp8_tile_slots(int M, int K) {
+  return (int64_t)((M + kTileRows - 1) / kTileRows) * ((K + kFp8TileStepK - 1) / kFp8TileStepK) * 64;
+}
+
 bool shape_ok(int M, int K) {
   return M >= 1 && K >= 32 && K % 32 == 0 && K <= (1 << 24) && (uint64_t)M * (uint64_t)(K / 2) < (1ull << 40);
 }
@@ -139,6 +195,35 @@ wq_status wq_nvfp4_untile(const uint8_t* tiled, int M, int K, uint8_t* codes, ui
   const int grid = (int)((slots + wq::kTileThreads - 1) / wq::kTileThreads);
   hipLaunchKernelGGL(wq::untile_kernel, dim3(grid), dim3(wq::kTileThreads), 0, static_cast<hipStream_t>(stream), tiled,
                      M, K, codes, scales, slots);
+  return hipGetLastError() == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+size_t wq_fp8_tiled_bytes(int M, int K) {
+  if (!wq::fp8_shape_ok(M, K)) return 0;
+  return (size_t)(wq::fp8_tile_slots(M, K) / 64) * wq::kFp8TileBlockBytes;
+}
+
+wq_status wq_fp8_tile(const uint8_t* w, int M, int K, uint8_t* tiled, void* stream) {
+  if (!w || !tiled) return WQ_ERROR_INVALID_VALUE;
+  if (M < 1 || K < 1) return WQ_ERROR_INVALID_VALUE;
+  if (!wq::fp8_shape_ok(M, K)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  if (((uintptr_t)w & 15u) || ((uintptr_t)tiled & 15u)) return WQ_ERROR_MISALIGNED;
+  const int64_t slots = wq::fp8_tile_slots(M, K);
+  const int grid = (int)((slots + wq::kTileThreads - 1) / wq::kTileThreads);
+  hipLaunchKernelGGL(wq::fp8_tile_kernel, dim3(grid), dim3(wq::kTileThreads), 0, static_cast<hipStream_t>(stream), w,
+                     M, K, tiled, slots);
+  return hipGetLastError() == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+wq_status wq_fp8_untile(const uint8_t* tiled, int M, int K, uint8_t* w, void* stream) {
+  if (!w || !tiled) return WQ_ERROR_INVALID_VALUE;
+  if (M < 1 || K < 1) return WQ_ERROR_INVALID_VALUE;
+  if (!wq::fp8_shape_ok(M, K)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  if (((uintptr_t)w & 15u) || ((uintptr_t)tiled & 15u)) return WQ_ERROR_MISALIGNED;
+  const int64_t slots = wq::fp8_tile_slots(M, K);
+  const int grid = (int)((slots + wq::kTileThreads - 1) / wq::kTileThreads);
+  hipLaunchKernelGGL(wq::fp8_untile_kernel, dim3(grid), dim3(wq::kTileThreads), 0, static_cast<hipStream_t>(stream),
+                     tiled, M, K, w, slots);
   return hipGetLastError() == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
 }
 

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libwq.so")
 WQ_FMT_NVFP4 = 0
 WQ_FMT_FP8ROW = 1
 WQ_FMT_NVFP4_TILED = 2
+WQ_FMT_FP8ROW_TILED = 3
 
 STATUS_NAMES = {
     0: "WQ_SUCCESS",
@@ -95,8 +96,17 @@ _lib.wq_nvfp4_untile.restype = _I
 _lib.wq_nvfp4_untile.argtypes = [_P, _I, _I, _P, _P, _P]
 _lib.wq_gemm_nvfp4_tiled.restype = _I
 _lib.wq_gemm_nvfp4_tiled.argtypes = [_P, ctypes.c_float, _P, _P, _I, _I, _I, _P, _S, _P]
+_lib.wq_fp8_tiled_bytes.restype = _S
+_lib.wq_fp8_tiled_bytes.argtypes = [_I, _I]
+_lib.wq_fp8_tile.restype = _I
+_lib.wq_fp8_tile.argtypes = [_P, _I, _I, _P, _P]
+_lib.wq_fp8_untile.restype = _I
+_lib.wq_fp8_untile.argtypes = [_P, _I, _I, _P, _P]
+_lib.wq_gemm_fp8row_tiled.restype = _I
+_lib.wq_gemm_fp8row_tiled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _S, _P]
 
 EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
+            "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
@@ -278,3 +288,35 @@ def wq_probe_copy(src, dst, stream=None, nbytes: Optional[int] = None):
 def wq_verify_launch(plan: WqVerifyPlan, stream=None):
     """Launch a prepared pass (kernel launch only)."""
     _check(_lib.wq_verify_launch(ctypes.byref(plan), _stream(stream)), "wq_verify_launch")
+
+
+def wq_fp8_tiled_bytes(M: int, K: int) -> int:
+    return int(_lib.wq_fp8_tiled_bytes(M, K))
+
+
+def wq_fp8_tile(w, tiled, stream=None, M: Optional[int] = None, K: Optional[int] = None):
+    """Permute plain FP8-row bytes (uint8 [M, K]) into the tiled layout (on the GPU)."""
+    if M is None:
+        M = w.shape[0]
+    if K is None:
+        K = w.shape[1]
+    _check(_lib.wq_fp8_tile(_ptr(w), M, K, _ptr(tiled), _stream(stream)), "wq_fp8_tile")
+
+
+def wq_fp8_untile(tiled, w, stream=None, M: Optional[int] = None, K: Optional[int] = None):
+    """Inverse of wq_fp8_tile."""
+    if M is None:
+        M = w.shape[0]
+    if K is None:
+        K = w.shape[1]
+    _check(_lib.wq_fp8_untile(_ptr(tiled), M, K, _ptr(w), _stream(stream)), "wq_fp8_untile")
+
+
+def wq_gemm_fp8row_tiled(tiled, row_scale, x, y, M: int, K: int, workspace=None, stream=None,
+                         N: Optional[int] = None, workspace_bytes: Optional[int] = None):
+    """y[N, M] = x[N, K] . W^T for row-scaled FP8 W in the tiled layout."""
+    if N is None:
+        N = x.shape[0]
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_gemm_fp8row_tiled(_ptr(tiled), _ptr(row_scale), _ptr(x), _ptr(y), M, K, N, _ptr(workspace), wsb,
+                                     _stream(stream)), "wq_gemm_fp8row_tiled")

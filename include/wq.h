@@ -60,13 +60,14 @@ typedef enum wq_status {
   WQ_ERROR_DEVICE = 6             /* no current HIP device, or not a gfx950 device */
 } wq_status;
 
-enum { WQ_FMT_NVFP4 = 0, WQ_FMT_FP8ROW = 1, WQ_FMT_NVFP4_TILED = 2 };
+enum { WQ_FMT_NVFP4 = 0, WQ_FMT_FP8ROW = 1, WQ_FMT_NVFP4_TILED = 2, WQ_FMT_FP8ROW_TILED = 3 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* wq_status_string(wq_status s);
 
-/* Bytes of workspace wq_gemm_nvfp4 (fmt = WQ_FMT_NVFP4) or wq_gemm_fp8row
- * (fmt = WQ_FMT_FP8ROW) needs for this shape on the current device; 0 when
+/* Bytes of workspace the single-matrix call of format `fmt` needs
+ * (wq_gemm_nvfp4, wq_gemm_fp8row, wq_gemm_nvfp4_tiled or
+ * wq_gemm_fp8row_tiled) for this shape on the current device; 0 when
  * the shape is computed without splitting K.  Returns 0 for invalid
  * arguments too (the GEMM call then reports the error). */
 size_t wq_gemm_workspace_bytes(int fmt, int M, int K, int N);
@@ -136,11 +137,36 @@ wq_status wq_gemm_fp8row(const uint8_t* w, const float* row_scale,
                          const uint16_t* x, float* y, int M, int K, int N,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Tiled FP8-row: the same E4M3 bytes, permuted once at load time so that
+ * every wave load is one contiguous kilobyte.  For T = ceil(M/16) row tiles
+ * and S = ceil(K/128) steps, block (t, s) is 2048 bytes at offset
+ * (t*S + s)*2048 and covers rows 16t..16t+15 and k = 128s..128s+127 (rows
+ * >= M and k >= K are zero bytes).  Inside it, with lane l = c + 16g
+ * (c = 0..15, g = 0..3) and h = 0..1:
+ *   bytes [1024h + 16l, +16) = plain bytes [128s + 64h + 16g, +16) of
+ *       row 16t + c.
+ * The row scales stay a separate FP32 array [M].
+ * wq_fp8_tiled_bytes: size of the tiled buffer (0 for an invalid shape).
+ * wq_fp8_tile / wq_fp8_untile: convert on the GPU (enqueue only; buffers
+ *   16-byte aligned, shapes as for wq_gemm_fp8row).  untile(tile(w))
+ *   reproduces w bit for bit.
+ * wq_gemm_fp8row_tiled: the product on tiled weights; same results as
+ *   wq_gemm_fp8row on the plain weights (bit for bit when wq_gemm_split
+ *   reports the same split for WQ_FMT_FP8ROW and WQ_FMT_FP8ROW_TILED). */
+size_t wq_fp8_tiled_bytes(int M, int K);
+wq_status wq_fp8_tile(const uint8_t* w, int M, int K, uint8_t* tiled, void* stream);
+wq_status wq_fp8_untile(const uint8_t* tiled, int M, int K, uint8_t* w, void* stream);
+wq_status wq_gemm_fp8row_tiled(const uint8_t* tiled, const float* row_scale,
+                               const uint16_t* x, float* y, int M, int K, int N,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* One matrix of a verify pass (host-side descriptor).  For WQ_FMT_NVFP4,
  * `w` = codes, `scales` = block scales, `global_scale` used; for
  * WQ_FMT_NVFP4_TILED, `w` = the tiled buffer, `scales` unused (may be
  * NULL), `global_scale` used; for WQ_FMT_FP8ROW, `w` = E4M3 codes,
- * `scales` = the FP32 row scales (reinterpreted), `global_scale` ignored.
+ * `scales` = the FP32 row scales (reinterpreted), `global_scale` ignored;
+ * for WQ_FMT_FP8ROW_TILED, `w` = the tiled buffer, `scales` = the row
+ * scales, `global_scale` ignored.
  * x [N][K], y [N][M] as above. */
 typedef struct wq_matrix {
   int32_t fmt;

@@ -106,3 +106,34 @@ def test_split_query_rejects_bad_args(wq):
     assert (kc.value, nc.value) == (5120, 1)
     assert lib.wq_gemm_split(1, 151936, 5120, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
     assert (kc.value, nc.value) == (5120, 1)
+
+
+def fp8t(lib, w=FAKE, rs=FAKE, x=FAKE, y=FAKE, M=64, K=128, N=4, ws=0, wsb=0):
+    return lib.wq_gemm_fp8row_tiled(w, rs, x, y, M, K, N, ws, wsb, 0)
+
+
+def test_fp8_tiled_argument_errors(wq):
+    lib = wq.lib()
+    INV, SHAPE, MIS = 1, 2, 3
+    assert fp8t(lib, w=0) == INV and fp8t(lib, rs=0) == INV and fp8t(lib, x=0) == INV and fp8t(lib, y=0) == INV
+    assert fp8t(lib, N=0) == INV and fp8t(lib, N=9) == INV and fp8t(lib, M=0) == INV
+    assert fp8t(lib, K=40) == SHAPE and fp8t(lib, K=8) == SHAPE
+    assert fp8t(lib, M=1 << 30, K=1 << 12) == SHAPE  # tiled buffer past 32-bit offsets
+    assert fp8t(lib, w=MISALIGNED) == MIS and fp8t(lib, rs=MISALIGNED) == MIS
+    # conversions: sizes, and errors before any launch
+    assert lib.wq_fp8_tiled_bytes(17, 48) == 2 * 1 * 2048
+    assert lib.wq_fp8_tiled_bytes(151936, 5120) == 9496 * 40 * 2048
+    assert lib.wq_fp8_tiled_bytes(16, 40) == 0 and lib.wq_fp8_tiled_bytes(0, 128) == 0
+    assert lib.wq_fp8_tile(0, 16, 128, FAKE, 0) == INV and lib.wq_fp8_tile(FAKE, 16, 128, 0, 0) == INV
+    assert lib.wq_fp8_tile(FAKE, 16, 40, FAKE, 0) == SHAPE and lib.wq_fp8_tile(MISALIGNED, 16, 128, FAKE, 0) == MIS
+    assert lib.wq_fp8_untile(FAKE, 16, 128, 0, 0) == INV and lib.wq_fp8_untile(FAKE, 16, 40, FAKE, 0) == SHAPE
+    # in a verify pass the tiled FP8 descriptor needs its row scales
+    good = wq.WqMatrix(3, 64, 128, 1.0, FAKE, FAKE, FAKE, FAKE)
+    arr = (wq.WqMatrix * 2)(good, good)
+    arr[1] = wq.WqMatrix(3, 64, 128, 1.0, FAKE, 0, FAKE, FAKE)
+    assert lib.wq_verify_pass(arr, 2, 4, FAKE, 1 << 20, 0) == INV
+    kc, nc = ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.wq_gemm_split(3, 151936, 5120, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (5120, 1)
+    assert lib.wq_gemm_split(3, 64, 17408, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (8704, 2)

@@ -1,14 +1,15 @@
-"""Tiled NVFP4 on the GPU: the conversion kernels match the layout's numpy
-statement byte for byte and invert exactly; the tiled product matches the
-oracle, and the plain product bit for bit when both use the same K split."""
+"""Tiled NVFP4 and tiled FP8-row on the GPU: the conversion kernels match
+the layouts' numpy statements byte for byte and invert exactly; the tiled
+products match the oracle, and the plain products bit for bit when both use
+the same K split."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from fp8_weight_streaming_amd import inputs
-from gpu_util import DEV, assert_close, dev_bf16bits, dev_u8, run_nvfp4, workspace
-from tiled_ref import tile_ref
+from gpu_util import DEV, assert_close, dev_bf16bits, dev_f32, dev_u8, run_fp8, run_nvfp4, workspace
+from tiled_ref import fp8_tile_ref, tile_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +126,134 @@ def test_tiled_verify_pass_column_invariance(wq):
         for N in range(1, 8):
             assert np.array_equal(outs[N][i].view(np.uint32), outs[8][i][:N].view(np.uint32)), \
                 "M=%d K=%d: N=%d differs from N=8" % (d.M, d.K, N)
+
+
+# ---- tiled FP8-row ------------------------------------------------------------
+
+def to_fp8_tiled(wq, d):
+    t = torch.empty(wq.wq_fp8_tiled_bytes(d.M, d.K), dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_tile(dev_u8(d.w), t)
+    return t
+
+
+def run_fp8_tiled(wq, d, N, x=None):
+    x = d.x if x is None else x
+    t = to_fp8_tiled(wq, d)
+    y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
+    ws = workspace(wq.wq_gemm_workspace_bytes(wq.WQ_FMT_FP8ROW_TILED, d.M, d.K, N))
+    wq.wq_gemm_fp8row_tiled(t, dev_f32(d.row_scale), dev_bf16bits(x[:N]), y, d.M, d.K, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+FP8_SHAPES = [(1, 16), (16, 128), (17, 48), (33, 208), (100, 544), (64, 1024), (250, 4240), (48, 8720),
+              (40, 17424), (5000, 5120)]
+
+
+@pytest.mark.parametrize("M,K", FP8_SHAPES)
+def test_fp8_tile_matches_layout_and_inverts(wq, M, K):
+    d = inputs.fp8row_inputs(M, K, 1, seed=500 + M + K)
+    t = to_fp8_tiled(wq, d)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), fp8_tile_ref(d.w)), "tiled bytes differ"
+    w = torch.zeros((M, K), dtype=torch.uint8, device=DEV)
+    wq.wq_fp8_untile(t, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(w.cpu().numpy(), d.w)
+
+
+@pytest.mark.parametrize("M,K", FP8_SHAPES[:-1])
+def test_fp8_tiled_gemm_all_n(wq, M, K):
+    d = inputs.fp8row_inputs(M, K, 8, seed=600 + M + K)
+    same = wq.wq_gemm_split(wq.WQ_FMT_FP8ROW, M, K) == wq.wq_gemm_split(wq.WQ_FMT_FP8ROW_TILED, M, K)
+    print("M=%d K=%d split plain=%s tiled=%s" % (M, K, wq.wq_gemm_split(1, M, K), wq.wq_gemm_split(3, M, K)),
+          flush=True)
+    for N in range(1, 9):
+        y = run_fp8_tiled(wq, d, N)
+        yr, ar = oracle.gemm_fp8row(d.w, d.row_scale, d.x[:N])
+        assert_close(y, yr, ar, "fp8 tiled M=%d K=%d N=%d" % (M, K, N))
+        if same:
+            yp = run_fp8(wq, d, N)
+            assert np.array_equal(yp.view(np.uint32), y.view(np.uint32)), "fp8 tiled vs plain bits N=%d" % N
+
+
+def test_fp8_tiled_edge_values(wq):
+    # NaN codes (S.1111.111) propagate only to their row; a zero row scale gives zeros
+    d = inputs.fp8row_inputs(40, 256, 8, seed=77)
+    d.w[3, 5] = 0x7F
+    d.w[21, 200] = 0xFF
+    d.row_scale[9] = 0.0
+    y = run_fp8_tiled(wq, d, 8)
+    yr, ar = oracle.gemm_fp8row(d.w, d.row_scale, d.x)
+    assert_close(y, yr, ar, "fp8 tiled edge values")
+    assert np.isnan(y[:, 3]).all() and np.isnan(y[:, 21]).all() and (y[:, 9] == 0).all()
+
+
+def test_fp8_tiled_column_invariance(wq):
+    d = inputs.fp8row_inputs(96, 17424, 8, seed=19)
+    y8 = run_fp8_tiled(wq, d, 8)
+    for N in (1, 3, 5, 7):
+        assert np.array_equal(run_fp8_tiled(wq, d, N).view(np.uint32), y8[:N].view(np.uint32))
+
+
+@pytest.mark.parametrize("N", [2, 8])
+def test_tiled_pass_nvfp4_and_fp8(wq, N):
+    # a dense layer in tiled NVFP4 next to a tiled FP8-row head slice, in one launch
+    mats, host, keep = [], [], []
+    for i, s in enumerate(inputs.VERIFY_LAYER):
+        d = inputs.nvfp4_inputs(s.M, s.K, N, seed=1300 + i, g=0.02)
+        t = to_tiled(wq, d)
+        y = torch.full((N, s.M), float("nan"), dtype=torch.float32, device=DEV)
+        x = dev_bf16bits(d.x)
+        mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, s.M, s.K, t, None, x, y, d.g))
+        host.append(("nvfp4", d))
+        keep.append((t, x))
+    d = inputs.fp8row_inputs(20000, 5120, N, seed=1310)
+    t, rs, x = to_fp8_tiled(wq, d), dev_f32(d.row_scale), dev_bf16bits(d.x)
+    y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
+    mats.append(wq.Matrix(wq.WQ_FMT_FP8ROW_TILED, d.M, d.K, t, rs, x, y, 1.0))
+    host.append(("fp8", d))
+    keep.append((t, rs, x))
+    ws = workspace(wq.wq_verify_workspace_bytes(mats, N))
+    wq.wq_verify_pass(mats, N, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(88 + N)
+    for m, (fmt, d) in zip(mats, host):
+        rows = np.unique(np.concatenate([rng.integers(0, m.M, 400), [0, m.M - 1]]))
+        if fmt == "nvfp4":
+            yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x, rows=rows)
+        else:
+            yr, ar = oracle.gemm_fp8row(d.w, d.row_scale, d.x, rows=rows)
+        assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "tiled pass %s M=%d K=%d N=%d" % (fmt, m.M, m.K, N))
+
+
+def test_mixed_pass_plain_and_tiled(wq):
+    # every format in one launch (the mixed kernel), small shapes with ragged tails
+    N = 5
+    mats, host, keep = [], [], []
+    dn = inputs.nvfp4_inputs(100, 544, N, seed=1400, g=0.02)
+    mats.append(wq.Matrix(wq.WQ_FMT_NVFP4, dn.M, dn.K, dev_u8(dn.codes), dev_u8(dn.scales), dev_bf16bits(dn.x),
+                          torch.full((N, dn.M), float("nan"), dtype=torch.float32, device=DEV), dn.g))
+    host.append(("nvfp4", dn))
+    dt = inputs.nvfp4_inputs(33, 17440, N, seed=1401, g=0.02)
+    mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, dt.M, dt.K, to_tiled(wq, dt), None, dev_bf16bits(dt.x),
+                          torch.full((N, dt.M), float("nan"), dtype=torch.float32, device=DEV), dt.g))
+    host.append(("nvfp4", dt))
+    df = inputs.fp8row_inputs(70, 208, N, seed=1402)
+    mats.append(wq.Matrix(wq.WQ_FMT_FP8ROW, df.M, df.K, dev_u8(df.w), dev_f32(df.row_scale), dev_bf16bits(df.x),
+                          torch.full((N, df.M), float("nan"), dtype=torch.float32, device=DEV), 1.0))
+    host.append(("fp8", df))
+    dg = inputs.fp8row_inputs(50, 17424, N, seed=1403)
+    mats.append(wq.Matrix(wq.WQ_FMT_FP8ROW_TILED, dg.M, dg.K, to_fp8_tiled(wq, dg), dev_f32(dg.row_scale),
+                          dev_bf16bits(dg.x), torch.full((N, dg.M), float("nan"), dtype=torch.float32, device=DEV),
+                          1.0))
+    host.append(("fp8", dg))
+    ws = workspace(wq.wq_verify_workspace_bytes(mats, N))
+    wq.wq_verify_pass(mats, N, ws)
+    torch.cuda.synchronize()
+    for m, (fmt, d) in zip(mats, host):
+        if fmt == "nvfp4":
+            yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x)
+        else:
+            yr, ar = oracle.gemm_fp8row(d.w, d.row_scale, d.x)
+        assert_close(m.y.cpu().numpy(), yr, ar, "mixed pass fmt=%d M=%d K=%d" % (m.fmt, m.M, m.K))

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from fp8_weight_streaming_amd import inputs
-from tiled_ref import tile_ref, untile_ref
+from tiled_ref import fp8_tile_ref, fp8_untile_ref, tile_ref, untile_ref
 
 
 @pytest.mark.parametrize("M,K", [(1, 32), (16, 256), (17, 96), (40, 544), (33, 1056)])
@@ -30,3 +30,24 @@ def test_tile_ref_places_bytes_as_documented():
     assert t[1, 1, 2048 + 8 * (16 + 3) + 4 + 1] == scales[19, 16 + 8 + 2 + 1]
     # padding rows (M = 20 < 32) are zero
     assert not t[1, :, :2048].reshape(2, 2, 64, 16)[:, :, [l for l in range(64) if (l & 15) >= 4], :].any()
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (16, 128), (17, 48), (40, 528), (33, 1040)])
+def test_fp8_tile_ref_round_trip(M, K):
+    d = inputs.fp8row_inputs(M, K, 1, seed=M * 5 + K)
+    t = fp8_tile_ref(d.w)
+    assert t.size == -(-M // 16) * -(-K // 128) * 2048
+    assert np.array_equal(fp8_untile_ref(t, M, K), d.w)
+
+
+def test_fp8_tile_ref_places_bytes_as_documented():
+    M, K = 20, 256
+    w = (np.arange(M * K, dtype=np.int64) % 253).astype(np.uint8).reshape(M, K)
+    t = fp8_tile_ref(w).reshape(2, 2, 2048)
+    # block (t=1, s=1), lane l = c + 16g with c=3, g=2, half h=1
+    c_, g_, h_ = 3, 2, 1
+    row, k0 = 16 + c_, 128 + 64 * h_ + 16 * g_
+    off = 1024 * h_ + 16 * (c_ + 16 * g_)
+    assert np.array_equal(t[1, 1, off:off + 16], w[row, k0:k0 + 16])
+    # every byte of the plain matrix appears exactly once; the rest is padding
+    assert np.array_equal(np.sort(t[t != 0]), np.sort(w[w != 0].reshape(-1)))

@@ -49,3 +49,33 @@ def untile_ref(tiled: np.ndarray, M: int, K: int):
     codes = cp.reshape(16 * T, 128 * S)[:M, :K // 2]
     scales = sp.reshape(16 * T, 16 * S)[:M, :K // 16]
     return np.ascontiguousarray(codes), np.ascontiguousarray(scales)
+
+
+def fp8_tile_ref(w: np.ndarray) -> np.ndarray:
+    """numpy statement of the tiled FP8-row layout documented in include/wq.h."""
+    M, K = w.shape
+    T, S = -(-M // 16), -(-K // 128)
+    wp = np.zeros((16 * T, 128 * S), np.uint8)
+    wp[:M, :K] = w
+    w4 = wp.reshape(T, 16, S, 128)          # [t][c][s][byte]
+    out = np.zeros((T, S, 2048), np.uint8)
+    for h in range(2):
+        for g in range(4):
+            src = 64 * h + 16 * g
+            for c in range(16):
+                dst = 1024 * h + 16 * (c + 16 * g)
+                out[:, :, dst:dst + 16] = w4[:, c, :, src:src + 16]
+    return out.reshape(-1)
+
+
+def fp8_untile_ref(tiled: np.ndarray, M: int, K: int) -> np.ndarray:
+    T, S = -(-M // 16), -(-K // 128)
+    b = tiled.reshape(T, S, 2048)
+    wp = np.zeros((T, 16, S, 128), np.uint8)
+    for h in range(2):
+        for g in range(4):
+            src = 64 * h + 16 * g
+            for c in range(16):
+                dst = 1024 * h + 16 * (c + 16 * g)
+                wp[:, c, :, src:src + 16] = b[:, :, dst:dst + 16]
+    return np.ascontiguousarray(wp.reshape(16 * T, 128 * S)[:M, :K])
