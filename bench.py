@@ -15,8 +15,11 @@ reported under "plain_layout".
 Printed: ONE JSON line with the metric (achieved HBM GB/s over the timed
 passes, algorithmic bytes per pass / pass time), the per-N breakdown, a
 roofline object for the verify kernel (HIP events on the launch stream),
-the CPU oracle's rate on a bounded sample, and a parity check of sampled
-output rows against the oracle.
+the CPU oracle's rate on a bounded sample, a parity check of sampled
+output rows against the oracle, and "single_products": the other four
+workloads (NVFP4 1024x1024 N=1, 17408x5120 N=1, 5120x17408 N=8, FP8-row
+151936x5120 N=8) as single calls, µs and GB/s per call for N = 1..8, each
+checked against the oracle (--no-single skips them).
 
     python bench.py [--gpus 1] [--steps 90] [--warmup 9]
 """
@@ -164,6 +167,126 @@ def cpu_baseline(wl, host, budget_s=12.0, max_layers=8):
                       "algorithmic in %.1f s" % (layers - 1, 4 * layers, nbytes / 1e9, dt)}
 
 
+# ---- the single-product configurations -------------------------------------------
+
+def matrix_bytes(fmt, M, K, N):
+    """Algorithmic bytes of one product: weights (NVFP4 0.5625 B, FP8 1 B
+    per weight plus 4 B per row scale), BF16 X, FP32 Y, 4 B tensor scale."""
+    if fmt == "nvfp4":
+        return M * K // 2 + M * K // 16 + 2 * N * K + 4 * N * M + 4
+    return M * K + 4 * M + 2 * N * K + 4 * N * M
+
+
+def single_products(wq, torch, stream, probe_gbps, check_rows=2048):
+    """Workloads 0, 1, 2 and 4 as single wq_gemm_* calls: for N = 1..8 on the
+    tiled layout and at the workload's own N on the plain layout.  Calls
+    run back to back over copies of the weights that together exceed 1 GiB
+    (more than the 256 MB last-level cache), each call bracketed by HIP
+    events on the launch stream; the median per-call time is reported.
+    At the workload's own N the output is checked against the oracle (all
+    rows, or check_rows sampled rows when M is larger), and that oracle call
+    is timed as the CPU figure of the row; at other N, 64 sampled rows."""
+    import oracle
+    dev = torch.device("cuda:0")
+    GiB = 1 << 30
+    out = []
+    for ci in (0, 1, 2, 4):
+        wl = inputs.workload(ci)
+        spec = wl.matrices[0]
+        M, K = spec.M, spec.K
+        # eight X columns for every workload (column 0 is the workload's own
+        # draw: X is drawn last, row-major)
+        if wl.fmt == "nvfp4":
+            d = inputs.nvfp4_inputs(M, K, NMAX, wl.seed(0), wl.g, wl.x_scale)
+        else:
+            d = inputs.fp8row_inputs(M, K, NMAX, wl.seed(0))
+        x8 = torch.from_numpy(d.x.view(np.int16)).to(dev)
+        if wl.fmt == "nvfp4":
+            codes, scales = torch.from_numpy(d.codes).to(dev), torch.from_numpy(d.scales).to(dev)
+            tb = wq.wq_nvfp4_tiled_bytes(M, K)
+            nt = max(2, -(-GiB // tb))
+            tiled = torch.empty((nt, tb), dtype=torch.uint8, device=dev)
+            wq.wq_nvfp4_tile(codes, scales, tiled[0], stream)
+            np_ = max(2, -(-GiB // (codes.numel() + scales.numel())))
+            pc = codes.view(1, -1).repeat(np_, 1)
+            ps = scales.view(1, -1).repeat(np_, 1)
+            fmt_t, fmt_p = wq.WQ_FMT_NVFP4_TILED, wq.WQ_FMT_NVFP4
+
+            def call_t(i, xN, y, ws):
+                wq.wq_gemm_nvfp4_tiled(tiled[i % nt], wl.g, xN, y, M, K, ws, stream)
+
+            def call_p(i, xN, y, ws):
+                wq.wq_gemm_nvfp4(pc[i % np_], ps[i % np_], wl.g, xN, y, ws, stream, M=M, K=K)
+
+            def ref(rows, N):
+                return oracle.gemm_nvfp4(d.codes, d.scales, wl.g, d.x[:N], rows=rows)
+        else:
+            w, rs = torch.from_numpy(d.w).to(dev), torch.from_numpy(d.row_scale).to(dev)
+            tb = wq.wq_fp8_tiled_bytes(M, K)
+            nt = max(2, -(-GiB // tb))
+            tiled = torch.empty((nt, tb), dtype=torch.uint8, device=dev)
+            wq.wq_fp8_tile(w, tiled[0], stream)
+            np_ = max(2, -(-GiB // w.numel()))
+            pw = w.view(1, -1).repeat(np_, 1)
+            fmt_t, fmt_p = wq.WQ_FMT_FP8ROW_TILED, wq.WQ_FMT_FP8ROW
+
+            def call_t(i, xN, y, ws):
+                wq.wq_gemm_fp8row_tiled(tiled[i % nt], rs, xN, y, M, K, ws, stream)
+
+            def call_p(i, xN, y, ws):
+                wq.wq_gemm_fp8row(pw[i % np_], rs, xN, y, ws, stream, M=M, K=K)
+
+            def ref(rows, N):
+                return oracle.gemm_fp8row(d.w, d.row_scale, d.x[:N], rows=rows)
+        for i in range(1, nt):
+            tiled[i].copy_(tiled[0])
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(777 + ci)
+        runs = [("tiled", fmt_t, call_t, nt, N) for N in range(1, NMAX + 1)] + [("plain", fmt_p, call_p, np_, wl.N)]
+        for layout, fmt, call, copies, N in runs:
+            xN = x8[:N]
+            y = torch.full((N, M), float("nan"), dtype=torch.float32, device=dev)
+            wsb = wq.wq_gemm_workspace_bytes(fmt, M, K, N)
+            ws = torch.zeros(wsb, dtype=torch.uint8, device=dev) if wsb else None
+            for i in range(3):
+                call(i, xN, y, ws)
+            reps = max(20, min(copies, 2000))
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            torch.cuda.synchronize()
+            for i in range(reps):
+                ev[i][0].record(stream)
+                call(3 + i, xN, y, ws)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+            nbytes = matrix_bytes(wl.fmt, M, K, N)
+            row = {"workload": ci, "name": wl.name, "N": N, "layout": layout, "split": list(wq.wq_gemm_split(fmt, M, K)),
+                   "us": us, "gbps": nbytes / us / 1e3, "pct_of_8TBps": 100 * nbytes / us / 1e3 / PEAK_GBPS,
+                   "pct_of_probe": 100 * nbytes / us / 1e3 / probe_gbps, "copies": copies}
+            own = N == wl.N
+            rows = np.arange(M) if (own and M <= check_rows) else np.unique(
+                np.concatenate([rng.integers(0, M, check_rows if own else 64), [0, M - 1]]))
+            yg = y.cpu().numpy()[:, rows].astype(np.float64)
+            t0 = time.perf_counter()
+            yr, ar = ref(rows, N)
+            t_or = time.perf_counter() - t0
+            err = np.abs(yg - yr)
+            bound = 1e-3 * ar
+            row["max_err_over_bound"] = float((err / np.maximum(bound, 1e-300)).max())
+            row["parity_ok"] = bool(not (err > bound).any() and np.array_equal(np.isnan(yg), np.isnan(yr)))
+            row["rows_checked"] = int(rows.size)
+            if own:
+                scale_rows = M / rows.size
+                row["oracle_us"] = t_or * scale_rows * 1e6
+                row["oracle_gbps"] = nbytes / (t_or * scale_rows) / 1e9
+                row["oracle_cores"] = oracle.num_threads()
+            out.append(row)
+            del y, ws
+        del tiled
+        torch.cuda.empty_cache()
+    return out
+
+
 # ---- main ------------------------------------------------------------------------
 
 def main():
@@ -174,6 +297,7 @@ def main():
     ap.add_argument("--layers", type=int, default=64, help="layers of the pass (64 is the measured workload)")
     ap.add_argument("--check-rows", type=int, default=32, help="sampled rows per matrix checked against the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single", action="store_true", help="skip the single-product workloads 0, 1, 2, 4")
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
     args = ap.parse_args()
 
@@ -330,6 +454,12 @@ def main():
     parity = {"ok": ok, "elements_checked": rows_checked, "max_err_over_bound": worst,
               "bound": "|y - y_oracle| <= 1e-3 * sum|w*x|"}
 
+    singles = None
+    if not args.no_single:
+        del plans_p
+        singles = single_products(wq, torch, stream, probe_gbps)
+        ok = ok and all(r["parity_ok"] for r in singles)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, host)
@@ -358,6 +488,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
+        "single_products": singles,
     }
     print(json.dumps(out))
     if not ok:
