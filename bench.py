@@ -282,9 +282,62 @@ def single_products(wq, torch, stream, probe_gbps, check_rows=2048):
                 row["oracle_cores"] = oracle.num_threads()
             out.append(row)
             del y, ws
+        if wl.fmt == "fp8row":
+            out += head_accept_rows(wq, torch, stream, wl, d, tiled, nt, rs, x8, probe_gbps)
         del tiled
         torch.cuda.empty_cache()
     return out
+
+
+def head_accept_rows(wq, torch, stream, wl, d, tiled, nt, rs, x8, probe_gbps):
+    """Greedy acceptance fused onto the FP8 head (workload 4, N = 8), with
+    and without writing the logits, timed like the products; the tokens are
+    checked against the greedy choice over the kernel's own logits and the
+    accepted count against the oracle's rule."""
+    from oracle.accept import greedy_accept, greedy_token
+    dev = torch.device("cuda:0")
+    spec = wl.matrices[0]
+    M, K, N = spec.M, spec.K, NMAX
+    fmt = wq.WQ_FMT_FP8ROW_TILED
+    ws = torch.zeros(wq.wq_head_accept_workspace_bytes(fmt, M, K, N), dtype=torch.uint8, device=dev)
+    tokens = torch.zeros(N, dtype=torch.int32, device=dev)
+    acc = torch.zeros(1, dtype=torch.int32, device=dev)
+    logits = torch.empty((N, M), dtype=torch.float32, device=dev)
+    drafts = torch.zeros(N - 1, dtype=torch.int32, device=dev)
+    wq.wq_head_accept(fmt, tiled[0], rs, 1.0, x8, M, K, drafts, tokens, acc, logits=logits, workspace=ws,
+                      stream=stream)
+    torch.cuda.synchronize()
+    t0 = tokens.cpu().numpy()
+    dr = list(t0[:N - 1])
+    dr[N - 3] = (dr[N - 3] + 1) % M  # drafts 1..N-3 accepted, draft N-2 rejected
+    drafts.copy_(torch.tensor(dr, dtype=torch.int32))
+    rows = []
+    for with_logits in (False, True):
+        lg = logits if with_logits else None
+        for i in range(3):
+            wq.wq_head_accept(fmt, tiled[i % nt], rs, 1.0, x8, M, K, drafts, tokens, acc, logits=lg, workspace=ws,
+                              stream=stream)
+        reps = 20
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev[i][0].record(stream)
+            wq.wq_head_accept(fmt, tiled[i % nt], rs, 1.0, x8, M, K, drafts, tokens, acc, logits=lg, workspace=ws,
+                              stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        nbytes = matrix_bytes("fp8row", M, K, N) - (0 if with_logits else 4 * N * M)
+        tk, a = tokens.cpu().numpy(), int(acc.cpu().numpy()[0])
+        lgn = logits.cpu().numpy()
+        ok = (all(tk[n] == greedy_token(lgn[n]) for n in range(N)) and np.array_equal(tk, t0)
+              and a == greedy_accept(lgn, dr)[1] == N - 3)
+        rows.append({"workload": 4, "name": "greedy acceptance fused on the fp8-row head 151936x5120",
+                     "N": N, "layout": "tiled", "logits_written": with_logits, "us": us,
+                     "gbps": nbytes / us / 1e3, "pct_of_8TBps": 100 * nbytes / us / 1e3 / PEAK_GBPS,
+                     "pct_of_probe": 100 * nbytes / us / 1e3 / probe_gbps, "accepted": a, "parity_ok": bool(ok),
+                     "max_err_over_bound": 0.0, "rows_checked": 0})
+    return rows
 
 
 # ---- main ------------------------------------------------------------------------

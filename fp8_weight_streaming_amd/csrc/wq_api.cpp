@@ -350,6 +350,40 @@ wq_status wq_gemm_fp8row_tiled(const uint8_t* tiled, const float* row_scale, con
   return gemm(kFmtFp8RowTiled, tiled, row_scale, 1.0f, x, y, M, K, N, workspace, workspace_bytes, stream);
 }
 
+size_t wq_head_accept_workspace_bytes(int fmt, int M, int K, int N) {
+  if (!is_tiled(fmt) || check_shape(fmt, M, K, N) != WQ_SUCCESS) return 0;
+  if (verify_split(fmt, M, K).nchunks != 1) return 0;
+  const int cus = current_cus();
+  if (cus <= 0) return 0;
+  return align_up((size_t)cus * 8 * sizeof(uint64_t), kAlign);
+}
+
+wq_status wq_head_accept(int fmt, const uint8_t* w, const float* row_scale, float global_scale, const uint16_t* x,
+                         int M, int K, int N, const int32_t* drafts, float* logits, int32_t* tokens,
+                         int32_t* accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!is_tiled(fmt)) return WQ_ERROR_INVALID_VALUE;
+  wq_status st = check_shape(fmt, M, K, N);
+  if (st != WQ_SUCCESS) return st;
+  if (!w || !x || !tokens || !accepted || (fmt == kFmtFp8RowTiled && !row_scale) || (N > 1 && !drafts))
+    return WQ_ERROR_INVALID_VALUE;
+  if (!aligned16(w) || !aligned16(x) || (row_scale && !aligned16(row_scale)) || (logits && !aligned16(logits)) ||
+      ((uintptr_t)tokens & 3u) || ((uintptr_t)accepted & 3u) || ((uintptr_t)drafts & 3u))
+    return WQ_ERROR_MISALIGNED;
+  const Split sp = verify_split(fmt, M, K);
+  if (sp.nchunks != 1) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  const int cus = current_cus();
+  if (cus <= 0) return WQ_ERROR_DEVICE;
+  const int grid = (int)std::min<int64_t>(cus, sp.ntiles);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < (size_t)grid * 8 * sizeof(uint64_t))
+    return WQ_ERROR_WORKSPACE;
+  DevMat one = dev_mat(fmt, w, row_scale, global_scale, x, logits, M, K, sp, nullptr, N, 0);
+  one.best = static_cast<uint64_t*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_stream(N, kModeTiledArgmax, nullptr, nullptr, one, grid, lds_bytes_for(N) + kArgLdsBytes, s);
+  if (e == hipSuccess) e = launch_accept(one.best, grid, N, drafts, tokens, accepted, s);
+  return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
 size_t wq_verify_workspace_bytes(const wq_matrix* descs, int count, int N) {
   if (check_descs(descs, count, N) != WQ_SUCCESS) return 0;
   const int cus = current_cus();

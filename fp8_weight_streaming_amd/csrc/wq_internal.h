@@ -50,7 +50,10 @@ __host__ __device__ constexpr uint32_t kZeroOffset() { return (uint32_t)kKcMax *
 template <int N>
 __host__ __device__ constexpr uint32_t kZeroBytes() { return 512u * N; }
 constexpr uint32_t lds_bytes_for(int n) { return (uint32_t)kKcMax * 2u * n + 512u * n; }
-constexpr uint32_t kMaxLdsBytes = lds_bytes_for(8);
+// Head acceptance (kModeTiledArgmax) adds, past the zero block, each wave's
+// best keys: 8 waves x 8 columns x 8 bytes.
+constexpr uint32_t kArgLdsBytes = 512;
+constexpr uint32_t kMaxLdsBytes = lds_bytes_for(8) + kArgLdsBytes;
 // idle-lane reads: tiled NVFP4 at 256N + 192N + 16, plain NVFP4 at 192N + 16,
 // FP8-row at 16N + 16 bytes past the zero block's start
 static_assert(kZeroBytes<1>() >= 448u * 1 + 16u && kZeroBytes<8>() >= 448u * 8 + 16u, "zero block too small");
@@ -70,6 +73,7 @@ struct DevMat {
   int nchunks;
   int ntiles;         // ceil(M / 16)
   int64_t unit0;      // index of this matrix's first unit in the pass
+  uint64_t* best;     // head acceptance: greedy keys [workgroup][8] (null otherwise)
 };
 
 // First unit (and the matrix holding it) of each workgroup's run.
@@ -96,15 +100,22 @@ constexpr int kModeNvfp4 = 1;         // NVFP4 only, any K % 32 == 0
 constexpr int kModeFp8 = 2;           // FP8-row only
 constexpr int kModeMixed = 3;         // any formats
 constexpr int kModeTiled = 4;         // tiled NVFP4 and tiled FP8-row only
+constexpr int kModeTiledArgmax = 5;   // one tiled matrix, greedy keys per workgroup (head acceptance)
 
 template <int MODE>
-__host__ __device__ constexpr int threads_for_mode() { return MODE == kModeTiled ? kThreadsTiled : kThreads; }
-constexpr int waves_for_mode(int mode) { return (mode == kModeTiled ? kThreadsTiled : kThreads) / 64; }
+__host__ __device__ constexpr int threads_for_mode() {
+  return (MODE == kModeTiled || MODE == kModeTiledArgmax) ? kThreadsTiled : kThreads;
+}
+constexpr int waves_for_mode(int mode) {
+  return ((mode == kModeTiled || mode == kModeTiledArgmax) ? kThreadsTiled : kThreads) / 64;
+}
 
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevMat& one, int grid, int N,
                          hipStream_t stream);
+hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t* drafts, int32_t* tokens,
+                         int32_t* accepted, hipStream_t stream);
 
 }  // namespace wq
 

@@ -314,9 +314,34 @@ __device__ void nvfp4_unit(const DevMat& mt, int chunk, int tile, const char* ld
 // wave's whole share is one sequential stream, and it is streamed as ONE
 // sequence of steps: the ring keeps PF steps in flight across tile
 // boundaries.
-template <int N, int PF, bool FP8>
-__device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds) {
-  if (first >= end) return;
+// Greedy key of one logit: the order of (value, -row) as an unsigned 64-bit
+// number, so that a max over keys gives the largest value and, among equal
+// values, the lowest row.  NaN sorts above every number (the first NaN row
+// wins) and -0 is taken as +0.
+__device__ __forceinline__ uint64_t greedy_key(float v, int m) {
+  uint32_t o;
+  if (v != v) {
+    o = 0xFFFFFFFFu;
+  } else {
+    const uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)m);
+}
+
+// ARG: also keep, per lane and register r, the greedy key of the lane's
+// outputs (lanes 0..31: column 4 * (lane / 16) + r, rows 16 t + lane % 16).
+//
+// stage() stages the run's X into LDS between two workgroup barriers.  The
+// run calls it once on every path, after issuing its first PF steps of
+// weight loads, so that their round trip overlaps the staging.
+template <int N, int PF, bool FP8, bool ARG, typename Stage>
+__device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds,
+                          uint64_t* bestk, Stage&& stage) {
+  if (first >= end) {
+    stage();
+    return;
+  }
   constexpr int kStep = FP8 ? kFp8TileStepK : kTileStepK;
   constexpr uint32_t kBlock = FP8 ? kFp8TileBlockBytes : kTileBlockBytes;
   const int lane = threadIdx.x & 63;
@@ -413,7 +438,8 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
   constexpr int kStores = N < 4 ? N : 4;
   const bool split = mt.nchunks > 1;
   float* const obase = split ? mt.part + (size_t)chunk * N * mt.M : mt.y;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc_uniform(obase, (uint64_t)N * (uint64_t)mt.M * 4u);
+  // (no output buffer -- head acceptance without logits -- drops every store)
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc_uniform(obase, obase ? (uint64_t)N * (uint64_t)mt.M * 4u : 0u);
   const float gscale = split ? 1.0f : mt.g;
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
   float prev[4] = {0.f, 0.f, 0.f, 0.f};
@@ -460,6 +486,12 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
                                                          false, false);
         sum[r] = __uint_as_float(lane < 32 ? q.x : q.y);
         prev[r] = cur;
+        if constexpr (ARG) {
+          const int mo = (tile0 + ci) * 16 + c;  // the lane's own row
+          const bool own = lane < 32 && mo < mt.M && 4 * (lane >> 4) + r < N;
+          const uint64_t key = own ? greedy_key(cur, mo) : 0ull;
+          bestk[r] = key > bestk[r] ? key : bestk[r];
+        }
         const int n = r + 4 * (lane >> 5);
         const bool live = emit && half_ok && m < mt.M && n < N;
         so[r] = live ? (uint32_t)((n * mt.M + m) * 4) : kDropOffset;
@@ -482,6 +514,7 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
     for (int r = 0; r < kStores; ++r) bstore4(0.0f, ro, kDropOffset + 4u * (4 * i + r));
     load_next(i);
   }
+  stage();
   int q0 = 0;
   for (; q0 + PF <= Q; q0 += PF) {
 #pragma unroll
@@ -584,6 +617,8 @@ __global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const 
     mi = ranges[blockIdx.x].mat;
   }
 
+  uint64_t bestk[4] = {0ull, 0ull, 0ull, 0ull};  // head acceptance
+
   // zero block read by lanes whose A-operand slots must be zero
   for (int i = threadIdx.x; i < kZeroBytes<N>() / 16; i += blockDim.x)
     *reinterpret_cast<u32x4*>(lds + kZeroOffset<N>() + 16 * i) = u32x4{0u, 0u, 0u, 0u};
@@ -604,23 +639,39 @@ __global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const 
                       : mt.fmt == kFmtNvfp4       ? 128
                                                   : 64;
     const int kc_pad = ((klen + seg_k - 1) / seg_k) * (seg_k / 8);
-    __syncthreads();
-    stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
-    __syncthreads();
-    // tiled NVFP4: wave w takes the w-th of nwaves equal shares of the run's
-    // consecutive tiles
+    // every wave calls this once per run (the barriers protect the LDS
+    // still read by the previous run, then publish the new X)
+    auto stage = [&]() {
+      __syncthreads();
+      stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
+      __syncthreads();
+    };
+    // tiled formats: wave w takes the w-th of nwaves equal shares of the
+    // run's consecutive tiles
     const int64_t len = run_end - u;
     const int64_t share0 = u + len * wave / nwaves, share1 = u + len * (wave + 1) / nwaves;
     if constexpr (MODE == kModeTiled) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchTiled, true>(mt, chunk, share0, share1, lds);
+        tiled_run<N, kPrefetchTiled, true, false>(mt, chunk, share0, share1, lds, bestk, stage);
       else
-        tiled_run<N, kPrefetchTiled, false>(mt, chunk, share0, share1, lds);
+        tiled_run<N, kPrefetchTiled, false, false>(mt, chunk, share0, share1, lds, bestk, stage);
+    } else if constexpr (MODE == kModeTiledArgmax) {
+      if (mt.fmt == kFmtFp8RowTiled)
+        tiled_run<N, kPrefetchTiled, true, true>(mt, chunk, share0, share1, lds, bestk, stage);
+      else
+        tiled_run<N, kPrefetchTiled, false, true>(mt, chunk, share0, share1, lds, bestk, stage);
     } else {
+      // (written out rather than through stage(): a by-reference lambda on
+      // this path kept the descriptor out of scalar registers and made the
+      // 128-VGPR kernels spill)
+      __syncthreads();
+      stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
+      __syncthreads();
+      auto staged = []() {};
       if (MODE == kModeMixed && mt.fmt == kFmtNvfp4Tiled) {
-        tiled_run<N, 1, false>(mt, chunk, share0, share1, lds);
+        tiled_run<N, 1, false, false>(mt, chunk, share0, share1, lds, bestk, staged);
       } else if (MODE == kModeMixed && mt.fmt == kFmtFp8RowTiled) {
-        tiled_run<N, 1, true>(mt, chunk, share0, share1, lds);
+        tiled_run<N, 1, true, false>(mt, chunk, share0, share1, lds, bestk, staged);
       } else {
         for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
           const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
@@ -640,6 +691,33 @@ __global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const 
       }
     }
     u = run_end;
+  }
+
+  if constexpr (MODE == kModeTiledArgmax) {
+    // the wave's best row per column: over the 16 row lanes of each half
+    // (lanes 0..15 hold columns r, lanes 16..31 columns 4 + r) ...
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const uint64_t o = __shfl_xor(bestk[r], off);
+        bestk[r] = o > bestk[r] ? o : bestk[r];
+      }
+    // ... then over the waves (LDS past the zero block), one key per column
+    uint64_t* wb = reinterpret_cast<uint64_t*>(lds + kZeroOffset<N>() + kZeroBytes<N>());
+    if (lane == 0 || lane == 16)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wb[wave * 8 + (lane >> 2) + r] = bestk[r];
+    __syncthreads();
+    if (threadIdx.x < 8) {
+      uint64_t b = 0ull;
+      for (int w = 0; w < nwaves; ++w) {
+        const uint64_t o = wb[w * 8 + threadIdx.x];
+        b = o > b ? o : b;
+      }
+      one.best[(size_t)blockIdx.x * 8 + threadIdx.x] = b;
+    }
   }
 }
 
@@ -680,6 +758,49 @@ hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevM
   return hipGetLastError();
 }
 
+// ---- greedy draft acceptance -------------------------------------------------
+// keys [groups][8]: each workgroup's best greedy key per column.  Column n's
+// target token is the row of the largest key; draft j (j = 1..N-1) is
+// accepted while it equals the token of column j - 1.
+constexpr int kAcceptThreads = 512;
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(const uint64_t* __restrict__ keys, int groups, int N,
+                                                               const int32_t* __restrict__ drafts,
+                                                               int32_t* __restrict__ tokens,
+                                                               int32_t* __restrict__ accepted) {
+  __shared__ int32_t tok[8];
+  const int n = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (n < N) {
+    uint64_t b = 0ull;
+    for (int g = lane; g < groups; g += 64) {
+      const uint64_t o = keys[(size_t)g * 8 + n];
+      b = o > b ? o : b;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t o = __shfl_xor(b, off);
+      b = o > b ? o : b;
+    }
+    if (lane == 0) {
+      const int32_t t = (int32_t)(0xFFFFFFFFu - (uint32_t)(b & 0xFFFFFFFFull));
+      tok[n] = t;
+      tokens[n] = t;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0;
+    while (a < N - 1 && drafts[a] == tok[a]) ++a;
+    accepted[0] = a;
+  }
+}
+
+hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t* drafts, int32_t* tokens,
+                         int32_t* accepted, hipStream_t stream) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(kAcceptThreads), 0, stream, keys, groups, N, drafts, tokens,
+                     accepted);
+  return hipGetLastError();
+}
+
 // ---- host-side launchers ---------------------------------------------------
 template <int N, int MODE>
 static hipError_t launch_nm(const DevMat* mats, const WgRange* ranges, const DevMat& one, int grid,
@@ -705,6 +826,7 @@ static hipError_t launch_n(int mode, const DevMat* mats, const WgRange* ranges, 
     case kModeFp8: return launch_nm<N, kModeFp8>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeMixed: return launch_nm<N, kModeMixed>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeTiled: return launch_nm<N, kModeTiled>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeTiledArgmax: return launch_nm<N, kModeTiledArgmax>(mats, ranges, one, grid, lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -102,11 +102,16 @@ _lib.wq_fp8_tile.restype = _I
 _lib.wq_fp8_tile.argtypes = [_P, _I, _I, _P, _P]
 _lib.wq_fp8_untile.restype = _I
 _lib.wq_fp8_untile.argtypes = [_P, _I, _I, _P, _P]
+_lib.wq_head_accept_workspace_bytes.restype = _S
+_lib.wq_head_accept_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.wq_head_accept.restype = _I
+_lib.wq_head_accept.argtypes = [_I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P]
 _lib.wq_gemm_fp8row_tiled.restype = _I
 _lib.wq_gemm_fp8row_tiled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _S, _P]
 
 EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
+            "wq_head_accept_workspace_bytes", "wq_head_accept",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
@@ -320,3 +325,20 @@ def wq_gemm_fp8row_tiled(tiled, row_scale, x, y, M: int, K: int, workspace=None,
     wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     _check(_lib.wq_gemm_fp8row_tiled(_ptr(tiled), _ptr(row_scale), _ptr(x), _ptr(y), M, K, N, _ptr(workspace), wsb,
                                      _stream(stream)), "wq_gemm_fp8row_tiled")
+
+
+def wq_head_accept_workspace_bytes(fmt: int, M: int, K: int, N: int) -> int:
+    return int(_lib.wq_head_accept_workspace_bytes(fmt, M, K, N))
+
+
+def wq_head_accept(fmt: int, w, row_scale, global_scale: float, x, M: int, K: int, drafts, tokens, accepted,
+                   logits=None, workspace=None, stream=None, N: Optional[int] = None,
+                   workspace_bytes: Optional[int] = None):
+    """Greedy acceptance on a tiled head: tokens[N] = per-column greedy rows,
+    accepted[1] = leading drafts equal to the previous column's token."""
+    if N is None:
+        N = x.shape[0]
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_head_accept(fmt, _ptr(w), _ptr(row_scale), float(global_scale), _ptr(x), M, K, N, _ptr(drafts),
+                               _ptr(logits), _ptr(tokens), _ptr(accepted), _ptr(workspace), wsb, _stream(stream)),
+           "wq_head_accept")

@@ -224,6 +224,40 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N,
                             wq_verify_plan* plan);
 wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream);
 
+/* Greedy draft acceptance fused onto the output-head product (the crit
+ * README, section "Core": greedy draft acceptance is part of sampling;
+ * section "Inference": speculative decoding verifies a proposed
+ * continuation and keeps the accepted tokens; the crit-hub engine card,
+ * section "Design", rows "Decode" and "Exactness": the verify pass runs
+ * inside the round's device graph, so the host never waits mid-round, and
+ * the output equals plain greedy decoding).
+ *   fmt        WQ_FMT_FP8ROW_TILED (w = tiled head, row_scale = FP32 [M]) or
+ *              WQ_FMT_NVFP4_TILED (w = tiled head, global_scale used,
+ *              row_scale may be NULL).  M = vocabulary rows, K = hidden size.
+ *   x          [N][K] BF16: column 0 the hidden state after the last
+ *              accepted token, columns 1..N-1 after drafts 1..N-1.
+ *   drafts     [N-1] int32, device (may be NULL when N = 1): the drafted
+ *              token ids, draft j = drafts[j-1].
+ *   logits     [N][M] FP32, device, or NULL: if given, the head's output,
+ *              as wq_gemm_*_tiled writes it.
+ *   tokens     [N] int32, device: tokens[n] = the row m with the largest
+ *              logits[n][m]; the lowest such m on ties; a NaN logit counts
+ *              as larger than any number (the lowest NaN row wins); -0 and
+ *              +0 are equal.
+ *   accepted   [1] int32, device: the number a of leading drafts with
+ *              draft j == tokens[j-1] for j = 1..a (0 <= a <= N-1); the
+ *              round's output tokens are tokens[0..a].
+ * Requirements: as wq_gemm_*_tiled, with K in one K chunk (K <= 8704:
+ * wq_gemm_split(fmt, M, K, 1, ...) reports one chunk); tokens, accepted,
+ * drafts 4-byte aligned.  The workspace (wq_head_accept_workspace_bytes;
+ * no initialization needed) holds one key per workgroup and column.
+ * Enqueues two kernels on `stream`; nothing is read back to the host. */
+size_t wq_head_accept_workspace_bytes(int fmt, int M, int K, int N);
+wq_status wq_head_accept(int fmt, const uint8_t* w, const float* row_scale, float global_scale,
+                         const uint16_t* x, int M, int K, int N, const int32_t* drafts,
+                         float* logits, int32_t* tokens, int32_t* accepted,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement kernels (not part of the product; they price it).  The crit
  * README's Eval turns the GPU's measured bandwidth into a floor for each
  * kernel, and the NInfer README ships a standalone bandwidth probe; these

@@ -137,3 +137,23 @@ def test_fp8_tiled_argument_errors(wq):
     assert (kc.value, nc.value) == (5120, 1)
     assert lib.wq_gemm_split(3, 64, 17408, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
     assert (kc.value, nc.value) == (8704, 2)
+
+
+def head(lib, fmt=3, w=FAKE, rs=FAKE, x=FAKE, M=1000, K=1024, N=4, drafts=FAKE, logits=FAKE, tokens=FAKE,
+         accepted=FAKE, ws=FAKE, wsb=1 << 20):
+    return lib.wq_head_accept(fmt, w, rs, 1.0, x, M, K, N, drafts, logits, tokens, accepted, ws, wsb, 0)
+
+
+def test_head_accept_argument_errors(wq):
+    lib = wq.lib()
+    INV, SHAPE, MIS = 1, 2, 3
+    assert head(lib, fmt=1) == INV and head(lib, fmt=0) == INV          # tiled heads only
+    assert head(lib, w=0) == INV and head(lib, x=0) == INV
+    assert head(lib, tokens=0) == INV and head(lib, accepted=0) == INV
+    assert head(lib, rs=0) == INV                                        # FP8 head needs its row scales
+    assert head(lib, drafts=0) == INV and head(lib, N=9) == INV and head(lib, N=0) == INV
+    assert head(lib, K=40) == SHAPE
+    assert head(lib, K=17408) == SHAPE                                   # more than one K chunk
+    assert head(lib, tokens=FAKE + 2) == MIS and head(lib, logits=FAKE + 4) == MIS and head(lib, w=FAKE + 8) == MIS
+    assert lib.wq_head_accept_workspace_bytes(1, 1000, 1024, 4) == 0
+    assert lib.wq_head_accept_workspace_bytes(3, 1000, 17408, 4) == 0
