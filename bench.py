@@ -340,6 +340,57 @@ def head_accept_rows(wq, torch, stream, wl, d, tiled, nt, rs, x8, probe_gbps):
     return rows
 
 
+def quantizer_rows(wq, torch, stream, probe_gbps, check_rows=64):
+    """The load-time quantizers on BF16 weights of the FP8 head's shape
+    (151936x5120 -> row-scaled FP8) and of the up-projection's shape
+    (17408x5120 -> NVFP4), HIP-event medians over 10 calls; sampled rows are
+    checked bit for bit against the oracle's quantizers."""
+    from oracle.quant import quantize_fp8row, quantize_nvfp4
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    rows = []
+    for name, M, K in (("fp8row", 151936, 5120), ("nvfp4", 17408, 5120)):
+        w = (torch.randn((M, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+        if name == "fp8row":
+            q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            r = torch.empty(M, dtype=torch.float32, device=dev)
+            call = lambda: wq.wq_quantize_fp8row(w, q, r, stream)  # noqa: E731
+            nbytes = 2 * M * K + M * K + 4 * M
+            g = None
+        else:
+            g = float(np.float32(float(w.view(torch.bfloat16).abs().max()) / (6 * 448)))
+            c = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            sc = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+            call = lambda: wq.wq_quantize_nvfp4(w, g, c, sc, stream)  # noqa: E731
+            nbytes = 2 * M * K + M * K // 2 + M * K // 16
+        for _ in range(2):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        sel = np.unique(np.random.default_rng(7).integers(0, M, check_rows))
+        wh = w[torch.from_numpy(sel).to(dev)].cpu().numpy().view(np.uint16)
+        if name == "fp8row":
+            qr, rr = quantize_fp8row(wh)
+            ok = (np.array_equal(q[torch.from_numpy(sel).to(dev)].cpu().numpy(), qr)
+                  and np.array_equal(r.cpu().numpy()[sel].view(np.uint32), rr.view(np.uint32)))
+        else:
+            cr, sr = quantize_nvfp4(wh, np.float32(g))
+            idx = torch.from_numpy(sel).to(dev)
+            ok = np.array_equal(c[idx].cpu().numpy(), cr) and np.array_equal(sc[idx].cpu().numpy(), sr)
+        rows.append({"quantizer": name, "M": M, "K": K, "us": us, "gbps": nbytes / us / 1e3,
+                     "pct_of_8TBps": 100 * nbytes / us / 1e3 / PEAK_GBPS, "rows_checked": int(sel.size),
+                     "bit_exact": bool(ok)})
+        del w
+        torch.cuda.empty_cache()
+    return rows
+
+
 # ---- main ------------------------------------------------------------------------
 
 def main():
@@ -507,11 +558,13 @@ def main():
     parity = {"ok": ok, "elements_checked": rows_checked, "max_err_over_bound": worst,
               "bound": "|y - y_oracle| <= 1e-3 * sum|w*x|"}
 
-    singles = None
+    singles = quant = None
     if not args.no_single:
         del plans_p
         singles = single_products(wq, torch, stream, probe_gbps)
         ok = ok and all(r["parity_ok"] for r in singles)
+        quant = quantizer_rows(wq, torch, stream, probe_gbps)
+        ok = ok and all(r["bit_exact"] for r in quant)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -542,6 +595,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "single_products": singles,
+        "quantizers": quant,
     }
     print(json.dumps(out))
     if not ok:

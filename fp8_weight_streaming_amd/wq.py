@@ -106,12 +106,16 @@ _lib.wq_head_accept_workspace_bytes.restype = _S
 _lib.wq_head_accept_workspace_bytes.argtypes = [_I, _I, _I, _I]
 _lib.wq_head_accept.restype = _I
 _lib.wq_head_accept.argtypes = [_I, _P, _P, ctypes.c_float, _P, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P]
+_lib.wq_quantize_fp8row.restype = _I
+_lib.wq_quantize_fp8row.argtypes = [_P, _I, _I, _P, _P, _P]
+_lib.wq_quantize_nvfp4.restype = _I
+_lib.wq_quantize_nvfp4.argtypes = [_P, _I, _I, ctypes.c_float, _P, _P, _P]
 _lib.wq_gemm_fp8row_tiled.restype = _I
 _lib.wq_gemm_fp8row_tiled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _S, _P]
 
 EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
-            "wq_head_accept_workspace_bytes", "wq_head_accept",
+            "wq_head_accept_workspace_bytes", "wq_head_accept", "wq_quantize_fp8row", "wq_quantize_nvfp4",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
@@ -342,3 +346,23 @@ def wq_head_accept(fmt: int, w, row_scale, global_scale: float, x, M: int, K: in
     _check(_lib.wq_head_accept(fmt, _ptr(w), _ptr(row_scale), float(global_scale), _ptr(x), M, K, N, _ptr(drafts),
                                _ptr(logits), _ptr(tokens), _ptr(accepted), _ptr(workspace), wsb, _stream(stream)),
            "wq_head_accept")
+
+
+def wq_quantize_fp8row(w, q, row_scale, stream=None, M: Optional[int] = None, K: Optional[int] = None):
+    """BF16 bits [M, K] -> E4M3 bytes q [M, K] and FP32 row scales [M] (round to nearest)."""
+    if M is None:
+        M = w.shape[0]
+    if K is None:
+        K = w.shape[1]
+    _check(_lib.wq_quantize_fp8row(_ptr(w), M, K, _ptr(q), _ptr(row_scale), _stream(stream)), "wq_quantize_fp8row")
+
+
+def wq_quantize_nvfp4(w, global_scale: float, codes, scales, stream=None, M: Optional[int] = None,
+                      K: Optional[int] = None):
+    """BF16 bits [M, K] -> NVFP4 codes [M, K/2] and E4M3 block scales [M, K/16] (round to nearest)."""
+    if M is None:
+        M = w.shape[0]
+    if K is None:
+        K = w.shape[1]
+    _check(_lib.wq_quantize_nvfp4(_ptr(w), M, K, float(global_scale), _ptr(codes), _ptr(scales), _stream(stream)),
+           "wq_quantize_nvfp4")

@@ -258,6 +258,28 @@ wq_status wq_head_accept(int fmt, const uint8_t* w, const float* row_scale, floa
                          float* logits, int32_t* tokens, int32_t* accepted,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Load-time round-to-nearest quantizers on the GPU (the crit landing page,
+ * section on Models: post-training quantization to FP8 or NVFP4 by
+ * round-to-nearest; its Gemma case study re-encodes BF16 projections and
+ * the output head to FP8 at load; the crit-hub engine card, section
+ * "Model", re-encodes the draft layer as row-scaled FP8 and the output
+ * head as NVFP4).  Input w [M][K] BF16 bits, finite, row-major.
+ *  wq_quantize_fp8row: per row m, row_scale[m] = fp32(max_k |w| / 448) and
+ *    q[m][k] = E4M3(fp32(w[m][k] / row_scale[m])); a zero row gives scale 0
+ *    and zero bytes.  K % 16 == 0.
+ *  wq_quantize_nvfp4: with tensor scale g (finite, > 0; g = amax / (6*448)
+ *    uses the full scale range), per block of 16 k: scale byte
+ *    s = E4M3(fp32(max |w| / fp32(6 g))), d = fp32(e4m3(s) * g), and
+ *    code = E2M1(fp32(w / d)), all zero when d = 0; codes/scales in the
+ *    layout wq_gemm_nvfp4 takes.  K % 32 == 0.
+ * E4M3 and E2M1 round to nearest, ties to the even code, saturate at 448
+ * and 6, and keep the sign bit (a negative value that rounds to zero gives
+ * the negative-zero code).  Divisions are correctly rounded FP32.  All
+ * buffers 16-byte aligned; enqueue only. */
+wq_status wq_quantize_fp8row(const uint16_t* w, int M, int K, uint8_t* q, float* row_scale, void* stream);
+wq_status wq_quantize_nvfp4(const uint16_t* w, int M, int K, float global_scale,
+                            uint8_t* codes, uint8_t* scales, void* stream);
+
 /* Measurement kernels (not part of the product; they price it).  The crit
  * README's Eval turns the GPU's measured bandwidth into a floor for each
  * kernel, and the NInfer README ships a standalone bandwidth probe; these

@@ -157,3 +157,17 @@ def test_head_accept_argument_errors(wq):
     assert head(lib, tokens=FAKE + 2) == MIS and head(lib, logits=FAKE + 4) == MIS and head(lib, w=FAKE + 8) == MIS
     assert lib.wq_head_accept_workspace_bytes(1, 1000, 1024, 4) == 0
     assert lib.wq_head_accept_workspace_bytes(3, 1000, 17408, 4) == 0
+
+
+def test_quantizer_argument_errors(wq):
+    lib = wq.lib()
+    INV, SHAPE, MIS = 1, 2, 3
+    q8 = lib.wq_quantize_fp8row
+    assert q8(0, 16, 64, FAKE, FAKE, 0) == INV and q8(FAKE, 16, 64, 0, FAKE, 0) == INV
+    assert q8(FAKE, 16, 64, FAKE, 0, 0) == INV and q8(FAKE, 0, 64, FAKE, FAKE, 0) == INV
+    assert q8(FAKE, 16, 40, FAKE, FAKE, 0) == SHAPE and q8(MISALIGNED, 16, 64, FAKE, FAKE, 0) == MIS
+    q4 = lib.wq_quantize_nvfp4
+    assert q4(FAKE, 16, 64, 0.0, FAKE, FAKE, 0) == INV and q4(FAKE, 16, 64, -1.0, FAKE, FAKE, 0) == INV
+    assert q4(FAKE, 16, 64, float("inf"), FAKE, FAKE, 0) == INV and q4(FAKE, 16, 64, float("nan"), FAKE, FAKE, 0) == INV
+    assert q4(0, 16, 64, 1.0, FAKE, FAKE, 0) == INV and q4(FAKE, 16, 48, 1.0, FAKE, FAKE, 0) == SHAPE
+    assert q4(FAKE, 16, 64, 1.0, FAKE + 8, FAKE, 0) == MIS
