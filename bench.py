@@ -391,6 +391,89 @@ def quantizer_rows(wq, torch, stream, probe_gbps, check_rows=64):
     return rows
 
 
+def draft_step_row(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=32):
+    """An N = 1 draft step on NVFP4 weights: one dense layer (layer 0 of the
+    pass, tiled) and an NVFP4 output head 151936x5120, re-encoded on the GPU
+    from BF16 by wq_quantize_nvfp4 and tiled, in one verify launch (the
+    crit README's case study drafts from NVFP4 copies of the draft layer
+    and head).  Sampled rows are checked against the oracle."""
+    import oracle
+    dev = torch.device("cuda:0")
+    M, K = 151936, 5120
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4343)
+    wb = (torch.randn((M, K), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    g = float(np.float32(float(wb.abs().max()) / (6 * 448)))
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    wq.wq_quantize_nvfp4(wb.view(torch.int16), g, codes, scales, stream)
+    del wb
+    head_t = torch.empty(wq.wq_nvfp4_tiled_bytes(M, K), dtype=torch.uint8, device=dev)
+    wq.wq_nvfp4_tile(codes, scales, head_t, stream)
+    xh = torch.from_numpy(inputs.to_bf16(np.random.default_rng(11).standard_normal((1, K)).astype(np.float32))
+                          .view(np.int16)).to(dev)
+    yh = torch.zeros((1, M), dtype=torch.float32, device=dev)
+    mats = [wq.Matrix(wq.WQ_FMT_NVFP4_TILED, s.M, s.K, t, None, x[:1], y[:1], wl.g)
+            for s, (c, sc, x, y, t) in zip(wl.matrices[:4], mats_dev[:4])]
+    mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, M, K, head_t, None, xh, yh, g))
+    ws = torch.zeros(wq.wq_verify_workspace_bytes(mats, 1), dtype=torch.uint8, device=dev)
+    plan = wq.wq_verify_prepare(mats, 1, ws, stream)
+    for _ in range(3):
+        wq.wq_verify_launch(plan, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in ev:
+        a.record(stream)
+        wq.wq_verify_launch(plan, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    nbytes = sum(matrix_bytes("nvfp4", m.M, m.K, 1) for m in mats)
+    rng = np.random.default_rng(99)
+    worst, ok = 0.0, True
+    ch, sh = codes.cpu().numpy(), scales.cpu().numpy()
+    for i, m in enumerate(mats):
+        rows = np.unique(np.concatenate([rng.integers(0, m.M, check_rows), [0, m.M - 1]]))
+        if i < 4:
+            d = host[i]
+            yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:1], rows=rows)
+        else:
+            yr, ar = oracle.gemm_nvfp4(ch, sh, g, xh.cpu().numpy().view(np.uint16), rows=rows)
+        yg = m.y.cpu().numpy()[:, rows].astype(np.float64)
+        err = np.abs(yg - yr)
+        ok = ok and not (err > 1e-3 * ar).any()
+        worst = max(worst, float((err / np.maximum(1e-3 * ar, 1e-300)).max()))
+    return {"name": "N=1 draft step: one dense layer + NVFP4 head 151936x5120 (GPU-quantized), one launch",
+            "matrices": len(mats), "us": us, "algorithmic_bytes": nbytes, "gbps": nbytes / us / 1e3,
+            "pct_of_8TBps": 100 * nbytes / us / 1e3 / PEAK_GBPS, "pct_of_probe": 100 * nbytes / us / 1e3 / probe_gbps,
+            "parity_ok": bool(ok), "max_err_over_bound": worst}
+
+
+def device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n, reps=9):
+    """The pass launched with its column count in device memory
+    (wq_verify_launch_n on one plan prepared for N = 8), per N."""
+    dev = torch.device("cuda:0")
+    mats = [wq.Matrix(wq.WQ_FMT_NVFP4_TILED, s.M, s.K, t, None, x, y, wl.g)
+            for s, (c, sc, x, y, t) in zip(wl.matrices, mats_dev)]
+    ws = torch.zeros(wq.wq_verify_workspace_bytes(mats, 8), dtype=torch.uint8, device=dev)
+    plan = wq.wq_verify_prepare(mats, 8, ws, stream)
+    n_dev = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for N in N_CYCLE:
+        n_dev.fill_(N)
+        for _ in range(4):
+            wq.wq_verify_launch_n(plan, n_dev, stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            wq.wq_verify_launch_n(plan, n_dev, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        out[str(N)] = {"us_per_pass_mean": us, "gbps": bytes_n[N] / us / 1e3,
+                       "pct_of_8TBps": 100 * bytes_n[N] / us / 1e3 / PEAK_GBPS}
+    return out
+
+
 # ---- main ------------------------------------------------------------------------
 
 def main():
@@ -558,8 +641,12 @@ def main():
     parity = {"ok": ok, "elements_checked": rows_checked, "max_err_over_bound": worst,
               "bound": "|y - y_oracle| <= 1e-3 * sum|w*x|"}
 
+    device_n = device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n)
+    draft = None
     singles = quant = None
     if not args.no_single:
+        draft = draft_step_row(wq, torch, stream, wl, host, mats_dev, probe_gbps)
+        ok = ok and draft["parity_ok"]
         del plans_p
         singles = single_products(wq, torch, stream, probe_gbps)
         ok = ok and all(r["parity_ok"] for r in singles)
@@ -594,6 +681,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
+        "per_n_device_count": device_n,
+        "draft_step": draft,
         "single_products": singles,
         "quantizers": quant,
     }

@@ -467,6 +467,22 @@ wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {
   return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
 }
 
+wq_status wq_verify_launch_n(const wq_verify_plan* plan, const int32_t* n_device, void* stream) {
+  if (!plan || !plan->workspace || !n_device || ((uintptr_t)n_device & 3u) || plan->N != 8 || plan->grid < 1 ||
+      plan->count < 1 || plan->mode != kModeTiled || plan->ranges_offset >= plan->workspace_bytes ||
+      plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes))
+    return WQ_ERROR_INVALID_VALUE;
+  const char* ws = static_cast<const char*>(plan->workspace);
+  const DevMat none{};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_stream_dyn(reinterpret_cast<const DevMat*>(ws),
+                                   reinterpret_cast<const WgRange*>(ws + plan->ranges_offset), n_device, plan->grid, s);
+  if (e == hipSuccess && plan->reduce_runs > 0)
+    e = launch_reduce(reinterpret_cast<const DevMat*>(ws), reinterpret_cast<const ReduceTask*>(ws + plan->reduce_offset),
+                      none, plan->reduce_runs, 8, s, n_device);
+  return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
 wq_status wq_verify_pass(const wq_matrix* descs, int count, int N, void* workspace, size_t workspace_bytes,
                          void* stream) {
   wq_verify_plan plan;

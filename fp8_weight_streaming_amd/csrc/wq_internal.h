@@ -113,7 +113,10 @@ constexpr int waves_for_mode(int mode) {
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevMat& one, int grid, int N,
-                         hipStream_t stream);
+                         hipStream_t stream, const int32_t* n_dev = nullptr);
+// the tiled verify pass with N read from n_dev (a plan prepared for N = 8)
+hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const int32_t* n_dev, int grid,
+                             hipStream_t stream);
 hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t* drafts, int32_t* tokens,
                          int32_t* accepted, hipStream_t stream);
 

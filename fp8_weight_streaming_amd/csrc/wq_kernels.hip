@@ -595,10 +595,8 @@ __device__ void fp8_unit(const DevMat& mt, int chunk, int tile, const char* lds)
 // global unit list (matrix-major, then chunk, then tile).  For a single
 // matrix (mats == nullptr) the split is computed here, equal by units.
 template <int N, int MODE>
-__global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const DevMat* __restrict__ mats,
-                                                          const WgRange* __restrict__ ranges,
-                                                          DevMat one) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+__device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, const WgRange* __restrict__ ranges,
+                                            const DevMat& one, char* lds) {
   // wave-uniform values are pinned to scalar registers so that buffer
   // resources built from them stay uniform
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -721,6 +719,50 @@ __global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const 
   }
 }
 
+template <int N, int MODE>
+__global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const DevMat* __restrict__ mats,
+                                                                          const WgRange* __restrict__ ranges,
+                                                                          DevMat one) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  stream_body<N, MODE>(mats, ranges, one, lds);
+}
+
+// The verify pass with the column count read from device memory (the
+// crit-hub engine card, section "Design", row "Decode": the round's graph
+// runs the verify pass for the drafts made, chosen on the device).  One
+// kernel holds the tiled pass for every N; the plan is the one for N = 8,
+// whose LDS, descriptors and partial-sum space cover every smaller N, and
+// the body for n computes exactly what stream_kernel<n, kModeTiled> does.
+__device__ __forceinline__ int device_n(const int32_t* n_dev) {
+  const int n = __builtin_amdgcn_readfirstlane(*n_dev);
+  return n < 1 ? 1 : n > 8 ? 8 : n;
+}
+
+// (inlined: as a called function each body needed a 280-byte stack frame
+// and ran slower)
+template <int N>
+__device__ __forceinline__ void dyn_body(const DevMat* __restrict__ mats, const WgRange* __restrict__ ranges,
+                                                   char* lds) {
+  const DevMat none{};
+  stream_body<N, kModeTiled>(mats, ranges, none, lds);
+}
+
+__global__ __launch_bounds__(kThreadsTiled) void stream_kernel_dyn(const DevMat* __restrict__ mats,
+                                                                   const WgRange* __restrict__ ranges,
+                                                                   const int32_t* __restrict__ n_dev) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  switch (device_n(n_dev)) {
+    case 1: dyn_body<1>(mats, ranges, lds); break;
+    case 2: dyn_body<2>(mats, ranges, lds); break;
+    case 3: dyn_body<3>(mats, ranges, lds); break;
+    case 4: dyn_body<4>(mats, ranges, lds); break;
+    case 5: dyn_body<5>(mats, ranges, lds); break;
+    case 6: dyn_body<6>(mats, ranges, lds); break;
+    case 7: dyn_body<7>(mats, ranges, lds); break;
+    default: dyn_body<8>(mats, ranges, lds); break;
+  }
+}
+
 // ---- split-K reduction -----------------------------------------------------
 // One thread per output (n, m) of a split matrix: y = scale * sum over chunks
 // of the partial sums, added in chunk order.  Block b handles outputs
@@ -728,7 +770,9 @@ __global__ __launch_bounds__(threads_for_mode<MODE>()) void stream_kernel(const 
 // matrix, mats == nullptr and the tasks are consecutive 4096-output runs).
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const DevMat* __restrict__ mats,
                                                                 const ReduceTask* __restrict__ tasks, DevMat one,
-                                                                int N) {
+                                                                int N, const int32_t* __restrict__ n_dev) {
+  // device N: the tasks were laid out for 8 columns; those past N * M end here
+  if (n_dev) N = device_n(n_dev);
   ReduceTask t;
   if (mats == nullptr) {
     const int64_t total = (int64_t)N * one.M;
@@ -740,6 +784,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const DevMat* __
   }
   const DevMat mt = mats ? mats[t.mat] : one;
   const int64_t plane = (int64_t)N * mt.M;
+  if (n_dev) t.count = (int32_t)max<int64_t>(0, min<int64_t>(t.count, plane - t.begin));
   for (int i = threadIdx.x; i < t.count; i += blockDim.x) {
     const int64_t o = t.begin + i;  // = n * M + m
     const int m = (int)(o % mt.M);
@@ -753,8 +798,22 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const DevMat* __
 }
 
 hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevMat& one, int grid, int N,
-                         hipStream_t stream) {
-  hipLaunchKernelGGL(reduce_kernel, dim3(grid), dim3(kReduceThreads), 0, stream, mats, tasks, one, N);
+                         hipStream_t stream, const int32_t* n_dev) {
+  hipLaunchKernelGGL(reduce_kernel, dim3(grid), dim3(kReduceThreads), 0, stream, mats, tasks, one, N, n_dev);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const int32_t* n_dev, int grid,
+                             hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel_dyn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(stream_kernel_dyn, dim3(grid), dim3(kThreadsTiled), lds_bytes_for(8), stream, mats, ranges,
+                     n_dev);
   return hipGetLastError();
 }
 

@@ -110,12 +110,15 @@ _lib.wq_quantize_fp8row.restype = _I
 _lib.wq_quantize_fp8row.argtypes = [_P, _I, _I, _P, _P, _P]
 _lib.wq_quantize_nvfp4.restype = _I
 _lib.wq_quantize_nvfp4.argtypes = [_P, _I, _I, ctypes.c_float, _P, _P, _P]
+_lib.wq_verify_launch_n.restype = _I
+_lib.wq_verify_launch_n.argtypes = [ctypes.POINTER(WqVerifyPlan), _P, _P]
 _lib.wq_gemm_fp8row_tiled.restype = _I
 _lib.wq_gemm_fp8row_tiled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _S, _P]
 
 EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
             "wq_head_accept_workspace_bytes", "wq_head_accept", "wq_quantize_fp8row", "wq_quantize_nvfp4",
+            "wq_verify_launch_n",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
@@ -366,3 +369,9 @@ def wq_quantize_nvfp4(w, global_scale: float, codes, scales, stream=None, M: Opt
         K = w.shape[1]
     _check(_lib.wq_quantize_nvfp4(_ptr(w), M, K, float(global_scale), _ptr(codes), _ptr(scales), _stream(stream)),
            "wq_quantize_nvfp4")
+
+
+def wq_verify_launch_n(plan: WqVerifyPlan, n_device, stream=None):
+    """Launch a plan prepared for N = 8 with the column count read from the
+    int32 device tensor n_device when the kernels run."""
+    _check(_lib.wq_verify_launch_n(ctypes.byref(plan), _ptr(n_device), _stream(stream)), "wq_verify_launch_n")

@@ -224,6 +224,18 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N,
                             wq_verify_plan* plan);
 wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream);
 
+/* The verify pass with its column count read from device memory when the
+ * kernels run (the crit-hub engine card, section "Design", row "Decode":
+ * the round's graph runs the verify pass for the drafts made, 2-8 columns,
+ * a number known only on the device).  `plan` must come from
+ * wq_verify_prepare with N = 8 over tiled matrices only (WQ_FMT_NVFP4_TILED
+ * and/or WQ_FMT_FP8ROW_TILED; the plan's x and y buffers hold 8 columns);
+ * `n_device` is an int32 in device memory, 4-byte aligned, read as
+ * n = min(max(*n_device, 1), 8).  Each matrix then gets y[0..n-1] =
+ * x[0..n-1] . W^T, bit for bit what a plan prepared for N = n computes;
+ * rows n..7 of y are left untouched.  Launch only (capture-safe). */
+wq_status wq_verify_launch_n(const wq_verify_plan* plan, const int32_t* n_device, void* stream);
+
 /* Greedy draft acceptance fused onto the output-head product (the crit
  * README, section "Core": greedy draft acceptance is part of sampling;
  * section "Inference": speculative decoding verifies a proposed

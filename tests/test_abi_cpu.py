@@ -171,3 +171,18 @@ def test_quantizer_argument_errors(wq):
     assert q4(FAKE, 16, 64, float("inf"), FAKE, FAKE, 0) == INV and q4(FAKE, 16, 64, float("nan"), FAKE, FAKE, 0) == INV
     assert q4(0, 16, 64, 1.0, FAKE, FAKE, 0) == INV and q4(FAKE, 16, 48, 1.0, FAKE, FAKE, 0) == SHAPE
     assert q4(FAKE, 16, 64, 1.0, FAKE + 8, FAKE, 0) == MIS
+
+
+def test_device_n_launch_argument_errors(wq):
+    lib = wq.lib()
+    plan = wq.WqVerifyPlan()
+    plan.workspace, plan.workspace_bytes, plan.count, plan.N, plan.mode, plan.grid = FAKE, 1 << 20, 2, 8, 4, 1
+    plan.ranges_offset = 256
+    import ctypes as C
+    assert lib.wq_verify_launch_n(None, FAKE, 0) == 1
+    assert lib.wq_verify_launch_n(C.byref(plan), 0, 0) == 1           # no device count
+    assert lib.wq_verify_launch_n(C.byref(plan), FAKE + 2, 0) == 1     # misaligned count
+    plan.N = 4
+    assert lib.wq_verify_launch_n(C.byref(plan), FAKE, 0) == 1         # plan not prepared for N = 8
+    plan.N, plan.mode = 8, 3
+    assert lib.wq_verify_launch_n(C.byref(plan), FAKE, 0) == 1         # not an all-tiled plan
