@@ -205,6 +205,7 @@ struct PassLayout {
   size_t table_bytes = 0, ranges_bytes = 0, tasks_bytes = 0, scratch_bytes = 0, total = 0;
   int grid = 0;
   int64_t units = 0;
+  int64_t dyn_chunks = 0;  // upper bound, for sizing (the tail holds at most all units)
 };
 
 wq_status check_descs(const wq_matrix* descs, int count, int N) {
@@ -235,7 +236,10 @@ PassLayout pass_layout(const wq_matrix* descs, int count, int N, int cus) {
       L.tasks.push_back(ReduceTask{b, i, (int32_t)std::min<int64_t>(kReduceRun, outs - b)});
   }
   L.table_bytes = align_up((size_t)count * sizeof(DevMat), kAlign);
-  L.ranges_bytes = align_up((size_t)(L.grid + 1) * sizeof(WgRange), kAlign);
+  L.dyn_chunks = ceil_div(L.units, kDynChunkMin);
+  L.ranges_bytes = align_up((size_t)(L.grid + 1) * sizeof(WgRange) + sizeof(DynSched) +
+                                (size_t)L.dyn_chunks * sizeof(int32_t),
+                            kAlign);
   L.tasks_bytes = align_up(L.tasks.size() * sizeof(ReduceTask), kAlign);
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
@@ -247,11 +251,21 @@ PassLayout pass_layout(const wq_matrix* descs, int count, int N, int cus) {
   return L;
 }
 
-// Splits the unit list into grid runs of (nearly) equal cost, where a
-// unit's cost is the weight bytes of its 16 rows in its K chunk plus a fixed
-// per-unit overhead.  Units of one (matrix, chunk) cost the same, so each
-// boundary inside such a group is found by division.
-std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout& L) {
+// Units per chunk of a pass's dynamic tail.
+int dyn_chunk_units(int64_t units, int grid) {
+  return (int)std::max<int64_t>(kDynChunkMin, std::min<int64_t>(kDynChunkMax, units / ((int64_t)grid * 32)));
+}
+
+// Splits the first (1 - kDynShare) of the pass's cost into grid runs of
+// (nearly) equal cost, where a unit's cost is the weight bytes of its 16
+// rows in its K chunk plus a fixed per-unit overhead; the rest of the unit
+// list is the dynamic tail (*dyn_begin onwards).  Units of one (matrix,
+// chunk) cost the same, so each boundary inside such a group is found by
+// division.  Only all-tiled passes of at least kDynMinUnitsPerWg units per
+// workgroup have a tail (smaller passes, and the plain-layout kernels, which
+// ramp up per unit, measured slower with one).
+std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout& L, bool tiled_only,
+                             int64_t* dyn_begin) {
   auto unit_cost = [&](int i, int c) {
     const Split& sp = L.splits[i];
     const int klen = std::min(sp.kc, descs[i].K - c * sp.kc);
@@ -261,17 +275,20 @@ std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout
   double total = 0.0;
   for (int i = 0; i < count; ++i)
     for (int c = 0; c < L.splits[i].nchunks; ++c) total += unit_cost(i, c) * L.splits[i].ntiles;
+  const bool tail = tiled_only && L.units >= (int64_t)L.grid * kDynMinUnitsPerWg;
+  const double stat = tail ? total * (1.0 - kDynShare) : total;
   std::vector<WgRange> ranges(L.grid + 1, WgRange{0, 0, 0});
   int w = 1;
   double acc = 0.0;
   int64_t u = 0;
+  const int last = tail ? L.grid : L.grid - 1;  // with a tail, range grid's end is a boundary too
   for (int i = 0; i < count; ++i) {
     const Split& sp = L.splits[i];
     for (int c = 0; c < sp.nchunks; ++c) {
       const double uc = unit_cost(i, c);
       const double end = acc + uc * sp.ntiles;
-      while (w < L.grid && total * w / L.grid < end) {
-        const double need = (total * w / L.grid - acc) / uc;
+      while (w <= last && stat * w / L.grid < end) {
+        const double need = (stat * w / L.grid - acc) / uc;
         int64_t j = need <= 0.0 ? 0 : (int64_t)std::ceil(need);
         if (j > sp.ntiles) j = sp.ntiles;
         ranges[w] = WgRange{u + j, i, 0};
@@ -283,6 +300,7 @@ std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout
   }
   for (; w <= L.grid; ++w) ranges[w] = WgRange{L.units, count - 1, 0};
   ranges[0] = WgRange{0, 0, 0};
+  *dyn_begin = ranges[L.grid].begin;
   return ranges;
 }
 
@@ -426,9 +444,27 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
       any_fp8 = true;
     }
   }
-  const std::vector<WgRange> ranges = balance(descs, count, L);
+  int64_t dyn_begin = L.units;
+  const std::vector<WgRange> ranges = balance(descs, count, L, any_tiled && !any_nv && !any_fp8, &dyn_begin);
   std::memcpy(host.data(), mats.data(), sizeof(DevMat) * count);
   std::memcpy(host.data() + L.table_bytes, ranges.data(), sizeof(WgRange) * ranges.size());
+  // the dynamic tail: its bounds, zeroed counters and each chunk's matrix
+  DynSched dyn{};
+  dyn.begin = dyn_begin;
+  dyn.end = L.units;
+  dyn.chunk = dyn_chunk_units(L.units, L.grid);
+  dyn.count = (int32_t)ceil_div(L.units - dyn_begin, dyn.chunk);
+  char* dyn_host = host.data() + L.table_bytes + sizeof(WgRange) * ranges.size();
+  std::memcpy(dyn_host, &dyn, sizeof(DynSched));
+  {
+    int32_t* cm = reinterpret_cast<int32_t*>(dyn_host + sizeof(DynSched));
+    int i = 0;
+    for (int32_t k = 0; k < dyn.count; ++k) {
+      const int64_t u0 = dyn_begin + (int64_t)k * dyn.chunk;
+      while (i + 1 < count && mats[i + 1].unit0 <= u0) ++i;
+      cm[k] = i;
+    }
+  }
   if (!L.tasks.empty())
     std::memcpy(host.data() + L.table_bytes + L.ranges_bytes, L.tasks.data(), sizeof(ReduceTask) * L.tasks.size());
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -83,6 +83,31 @@ struct WgRange {
   int32_t pad;
 };
 
+// The dynamic tail of a verify pass, stored right after the grid + 1
+// ranges: units [begin, end) are handed out in chunks of `chunk` units, in
+// order, to whichever workgroup asks next (an atomic counter), so that
+// workgroups that streamed their static range faster take more.  `next`
+// and `done` start at 0 (the plan's upload zeroes them); the last
+// workgroup to finish a launch sets them back to 0.  `chunk_mat` (count
+// entries) follows: the matrix holding each chunk's first unit.
+struct DynSched {
+  int64_t begin;
+  int64_t end;
+  int32_t chunk;
+  int32_t count;
+  uint32_t next;
+  uint32_t done;
+};
+// Share of a pass's cost left to the dynamic tail, and its chunk sizes:
+// units per workgroup / 32, within [8, 16] (16 for the dense 64-layer
+// pass).  A chunk's fixed cost (X restaging, the ring's ramp) wants it
+// large, the balance at the end wants it small next to a workgroup's work;
+// passes under kDynMinUnitsPerWg units per workgroup have no tail.
+constexpr double kDynShare = 0.08;
+constexpr int kDynChunkMin = 8;
+constexpr int kDynChunkMax = 16;
+constexpr int kDynMinUnitsPerWg = 256;
+
 // One run of outputs of a split matrix for reduce_kernel.
 struct ReduceTask {
   int64_t begin;  // first output index (n * M + m)

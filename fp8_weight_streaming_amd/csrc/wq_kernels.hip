@@ -621,6 +621,16 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
   for (int i = threadIdx.x; i < kZeroBytes<N>() / 16; i += blockDim.x)
     *reinterpret_cast<u32x4*>(lds + kZeroOffset<N>() + 16 * i) = u32x4{0u, 0u, 0u, 0u};
 
+  // a verify pass: after its static range the workgroup claims chunks of
+  // the dynamic tail until none is left
+  // (only the tiled kernel has the claim loop: plans of other kernels have no
+  // tail, and the loop's presence alone slowed the plain-layout kernels)
+  DynSched* const dyn = (MODE == kModeTiled && mats)
+                            ? reinterpret_cast<DynSched*>(const_cast<WgRange*>(ranges) + gridDim.x + 1)
+                            : nullptr;
+  __shared__ uint32_t s_claim;
+
+  for (;;) {
   while (u < u_end) {
     const DevMat mt = mats ? mats[mi] : one;
     const int64_t mend = mt.unit0 + (int64_t)mt.nchunks * mt.ntiles;
@@ -689,6 +699,23 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       }
     }
     u = run_end;
+  }
+  if (!dyn) break;
+  __syncthreads();  // every wave has read the previous claim
+  if (threadIdx.x == 0) s_claim = atomicAdd(&dyn->next, 1u);
+  __syncthreads();
+  const uint32_t idx = s_claim;
+  if (idx >= (uint32_t)dyn->count) break;
+  u = dyn->begin + (int64_t)idx * dyn->chunk;
+  u_end = min(u + (int64_t)dyn->chunk, dyn->end);
+  mi = reinterpret_cast<const int32_t*>(dyn + 1)[idx];
+  }
+  // The last workgroup to finish sets the counters back for the next launch.
+  // Every workgroup's final claim has returned before its `done` increment
+  // (its exit depends on the claim's value), so no claim can follow.
+  if (dyn && threadIdx.x == 0 && atomicAdd(&dyn->done, 1u) == gridDim.x - 1) {
+    atomicExch(&dyn->next, 0u);
+    atomicExch(&dyn->done, 0u);
   }
 
   if constexpr (MODE == kModeTiledArgmax) {
