@@ -257,3 +257,30 @@ def test_mixed_pass_plain_and_tiled(wq):
         else:
             yr, ar = oracle.gemm_fp8row(d.w, d.row_scale, d.x)
         assert_close(m.y.cpu().numpy(), yr, ar, "mixed pass fmt=%d M=%d K=%d" % (m.fmt, m.M, m.K))
+
+
+def test_dynamic_tail_covers_every_unit_on_every_launch(wq):
+    # A pass large enough (>= 256 units per workgroup) for the dynamic tail:
+    # two tiled matrices, so the tail crosses a matrix boundary.  Every output
+    # of every one of three launches (outputs reset to NaN in between) must
+    # match the oracle: a chunk claimed twice or never would show, and so
+    # would a counter not reset for the next launch.
+    N = 3
+    specs = [(600000, 256), (500000, 256)]
+    host = [inputs.nvfp4_inputs(M, K, N, seed=1900 + i, g=0.02) for i, (M, K) in enumerate(specs)]
+    mats = []
+    for d in host:
+        t = to_tiled(wq, d)
+        y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
+        mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, t, None, dev_bf16bits(d.x), y, d.g))
+    ws = workspace(wq.wq_verify_workspace_bytes(mats, N))
+    plan = wq.wq_verify_prepare(mats, N, ws)
+    refs = [oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x) for d in host]
+    for launch in range(3):
+        for m in mats:
+            m.y.fill_(float("nan"))
+        print("tail launch %d" % launch, flush=True)
+        wq.wq_verify_launch(plan)
+        torch.cuda.synchronize()
+        for m, (yr, ar) in zip(mats, refs):
+            assert_close(m.y.cpu().numpy(), yr, ar, "launch %d M=%d" % (launch, m.M))
