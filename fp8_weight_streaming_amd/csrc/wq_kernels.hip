@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "wq_internal.h"
 
 namespace wq {
@@ -830,15 +832,24 @@ hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevM
   return hipGetLastError();
 }
 
+// The dynamic-LDS limit of a kernel is raised once per device (the
+// attribute is per device; a bit per device ordinal, set after success).
+static hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const int32_t* n_dev, int grid,
                              hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel_dyn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&stream_kernel_dyn), lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(stream_kernel_dyn, dim3(grid), dim3(kThreadsTiled), lds_bytes_for(8), stream, mats, ranges,
                      n_dev);
   return hipGetLastError();
@@ -891,13 +902,9 @@ hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t*
 template <int N, int MODE>
 static hipError_t launch_nm(const DevMat* mats, const WgRange* ranges, const DevMat& one, int grid,
                             size_t lds_bytes, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&stream_kernel<N, MODE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&stream_kernel<N, MODE>), lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_kernel<N, MODE>), dim3(grid), dim3(threads_for_mode<MODE>()), lds_bytes, stream, mats,
                      ranges, one);
   return hipGetLastError();
