@@ -182,3 +182,39 @@ def workload_inputs(wl: Workload, matrix_index: int = 0):
     if wl.fmt == "nvfp4":
         return nvfp4_inputs(spec.M, spec.K, wl.N, wl.seed(matrix_index), wl.g, wl.x_scale)
     return fp8row_inputs(spec.M, spec.K, wl.N, wl.seed(matrix_index))
+
+
+# ---- chained MLP layers --------------------------------------------------
+
+# rms of the stored NVFP4 weight values drawn by nvfp4_inputs with g = 1:
+# E2M1 codes uniform over all 16 (mean square 68.5 / 8) times block scales
+# 2^U(-4, 2) (mean square (16 - 4^-4) / (6 ln 4)).
+NVFP4_DRAW_RMS = float(np.sqrt(68.5 / 8 * (16.0 - 4.0 ** -4) / (6.0 * np.log(4.0))))
+
+
+@dataclass
+class MlpLayerInputs:
+    gate: NVFP4Inputs   # [F][D]  (x unused)
+    up: NVFP4Inputs     # [F][D]
+    down: NVFP4Inputs   # [D][F]
+    gamma: np.ndarray   # uint16 [D] BF16 norm weights
+
+
+def mlp_layer_inputs(D: int, F: int, seed: int, down_gain: float = 0.25) -> MlpLayerInputs:
+    """Weights of one MLP layer.  Tensor scales put the gate/up outputs near
+    unit size for unit-size normalized inputs, and scale each layer's
+    addition to the residual by about down_gain, so that a stack of many
+    layers stays in range."""
+    g_gu = float(np.float32(1.0 / (NVFP4_DRAW_RMS * np.sqrt(D))))
+    g_d = float(np.float32(down_gain / (NVFP4_DRAW_RMS * np.sqrt(F))))
+    gate = nvfp4_inputs(F, D, 1, 4 * seed + 0, g_gu)
+    up = nvfp4_inputs(F, D, 1, 4 * seed + 1, g_gu)
+    down = nvfp4_inputs(D, F, 1, 4 * seed + 2, g_d)
+    rng = _rng(4 * seed + 3)
+    gamma = to_bf16((1.0 + 0.2 * rng.standard_normal(D)).astype(np.float32))
+    return MlpLayerInputs(gate, up, down, gamma)
+
+
+def residual_inputs(N: int, D: int, seed: int) -> np.ndarray:
+    """FP32 residual-stream columns [N][D]."""
+    return _rng(seed).standard_normal(size=(N, D), dtype=np.float32)
