@@ -304,6 +304,69 @@ std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout
   return ranges;
 }
 
+// ---- chained MLP layers --------------------------------------------------------
+// K split of a chain's down product (M = D rows, K = F), launched alone at 16
+// waves per workgroup, whose waves stream all of the workgroup's units at
+// once.  Candidates are scored by the busiest workgroup's units times steps
+// per unit (fewer than 8 units leave the CU's memory pipeline part idle, so
+// count as 8), plus half a step per chunk for the partial sums and their
+// reduction.
+Split chain_down_split(int D, int F, int cus) {
+  const int sk = kTileStepK;
+  const int64_t ntiles = ceil_div(D, kTileRows);
+  const int nmin = (int)ceil_div(F, kKcMax);
+  const int nmax = std::max(nmin, (int)std::min<int64_t>(32, ceil_div(F, sk)));
+  Split best = verify_split(kFmtNvfp4Tiled, D, F);
+  double best_cost = 1e300;
+  for (int n = nmin; n <= nmax; ++n) {
+    const int kc = (int)(ceil_div(ceil_div(F, n), sk) * sk);
+    if ((int)ceil_div(F, kc) != n) continue;  // same split as a smaller n
+    const int64_t units = ntiles * n;
+    const int64_t per = ceil_div(units, std::min<int64_t>(cus, units));
+    const double cost = (double)std::max<int64_t>(per, 8) * (kc / sk) + 0.5 * n;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = make_split(kFmtNvfp4Tiled, D, F, kc);
+    }
+  }
+  return best;
+}
+
+struct ChainLayout {
+  Split gate_up, down;
+  int grid_gate_up = 0, grid_down = 0, parts = 0;
+  size_t table_bytes = 0, ranges_gu_bytes = 0, ranges_down_bytes = 0, part_bytes = 0, ssp_bytes = 0, total = 0;
+};
+
+wq_status check_chain_shape(int layers, int D, int F, int N) {
+  if (layers < 1 || layers > (1 << 20) || N < 1 || N > 8 || D < 1 || F < 1) return WQ_ERROR_INVALID_VALUE;
+  if (D % 32 != 0 || F % 32 != 0 || D > kKcMax || F > (1 << 24)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  wq_status st = check_shape(kFmtNvfp4Tiled, 2 * F, D, N);
+  if (st != WQ_SUCCESS) return st;
+  return check_shape(kFmtNvfp4Tiled, D, F, N);
+}
+
+ChainLayout chain_layout(int layers, int D, int F, int N, int cus) {
+  ChainLayout L;
+  L.gate_up = verify_split(kFmtNvfp4Tiled, 2 * F, D);  // one chunk: D <= kKcMax
+  L.down = chain_down_split(D, F, cus);
+  L.grid_gate_up = (int)std::min<int64_t>(cus, L.gate_up.ntiles);
+  L.grid_down = (int)std::min<int64_t>(cus, (int64_t)L.down.ntiles * L.down.nchunks);
+  L.parts = (int)ceil_div(D, kChainThreads);
+  L.table_bytes = align_up((size_t)2 * layers * sizeof(DevMat), kAlign);
+  L.ranges_gu_bytes = align_up((size_t)(L.grid_gate_up + 1) * sizeof(WgRange), kAlign);
+  L.ranges_down_bytes = align_up((size_t)(L.grid_down + 1) * sizeof(WgRange), kAlign);
+  L.part_bytes = align_up((size_t)L.down.nchunks * N * D * sizeof(float), kAlign);
+  L.ssp_bytes = align_up((size_t)N * L.parts * sizeof(float), kAlign);
+  L.total = L.table_bytes + L.ranges_gu_bytes + L.ranges_down_bytes + L.part_bytes + L.ssp_bytes;
+  return L;
+}
+
+// grid runs of (nearly) equal unit counts over one matrix
+void equal_ranges(int64_t units, int grid, WgRange* out) {
+  for (int w = 0; w <= grid; ++w) out[w] = WgRange{units * w / grid, 0, 0};
+}
+
 }  // namespace
 }  // namespace wq
 
@@ -525,6 +588,127 @@ wq_status wq_verify_pass(const wq_matrix* descs, int count, int N, void* workspa
   wq_status st = wq_verify_prepare(descs, count, N, workspace, workspace_bytes, stream, &plan);
   if (st != WQ_SUCCESS) return st;
   return wq_verify_launch(&plan, stream);
+}
+
+size_t wq_mlp_chain_workspace_bytes(int layers, int D, int F, int N) {
+  if (check_chain_shape(layers, D, F, N) != WQ_SUCCESS) return 0;
+  const int cus = current_cus();
+  if (cus <= 0) return 0;
+  return chain_layout(layers, D, F, N, cus).total;
+}
+
+wq_status wq_mlp_chain_split(int D, int F, int* k_chunk, int* n_chunks) {
+  if (!k_chunk || !n_chunks) return WQ_ERROR_INVALID_VALUE;
+  wq_status st = check_chain_shape(1, D, F, 1);
+  if (st != WQ_SUCCESS) return st;
+  const int cus = current_cus();
+  if (cus <= 0) return WQ_ERROR_DEVICE;
+  const Split sp = chain_down_split(D, F, cus);
+  *k_chunk = sp.kc;
+  *n_chunks = sp.nchunks;
+  return WQ_SUCCESS;
+}
+
+wq_status wq_mlp_chain_prepare(const wq_mlp_layer* layers, int count, int D, int F, int N, float eps, float* h,
+                               uint16_t* a, uint16_t* s, void* workspace, size_t workspace_bytes, void* stream,
+                               wq_mlp_plan* plan) {
+  if (!plan || !layers) return WQ_ERROR_INVALID_VALUE;
+  wq_status st = check_chain_shape(count, D, F, N);
+  if (st != WQ_SUCCESS) return st;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return WQ_ERROR_INVALID_VALUE;
+  if (!h || !a || !s) return WQ_ERROR_INVALID_VALUE;
+  if (!aligned16(h) || !aligned16(a) || !aligned16(s)) return WQ_ERROR_MISALIGNED;
+  for (int l = 0; l < count; ++l) {
+    const wq_mlp_layer& y = layers[l];
+    if (!y.gate_up || !y.down || !y.gamma) return WQ_ERROR_INVALID_VALUE;
+    if (!aligned16(y.gate_up) || !aligned16(y.down) || !aligned16(y.gamma)) return WQ_ERROR_MISALIGNED;
+  }
+  if (!workspace) return WQ_ERROR_WORKSPACE;
+  if (!aligned16(workspace)) return WQ_ERROR_MISALIGNED;
+  const int cus = current_cus();
+  if (cus <= 0) return WQ_ERROR_DEVICE;
+  const ChainLayout L = chain_layout(count, D, F, N, cus);
+  if (workspace_bytes < L.total) return WQ_ERROR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const size_t off_rgu = L.table_bytes;
+  const size_t off_rdn = off_rgu + L.ranges_gu_bytes;
+  const size_t off_part = off_rdn + L.ranges_down_bytes;
+  const size_t off_ssp = off_part + L.part_bytes;
+  float* part = reinterpret_cast<float*>(ws + off_part);
+  float* ssp = reinterpret_cast<float*>(ws + off_ssp);
+
+  thread_local std::vector<char> host;
+  host.assign(off_part, 0);
+  DevMat* mats = reinterpret_cast<DevMat*>(host.data());
+  for (int l = 0; l < count; ++l) {
+    const wq_mlp_layer& y = layers[l];
+    DevMat g{};
+    g.w = static_cast<const uint8_t*>(y.gate_up);
+    g.fmt = kFmtNvfp4Tiled;
+    g.M = 2 * F;
+    g.K = D;
+    g.kc = L.gate_up.kc;
+    g.nchunks = 1;
+    g.ntiles = L.gate_up.ntiles;
+    g.g = y.gate_scale;
+    g.g2 = y.up_scale;
+    g.eps = eps;
+    g.h = h;
+    g.ssp = ssp;
+    g.nparts = L.parts;
+    g.gamma = y.gamma;
+    g.aout = a;
+    g.sout = s;
+    mats[2 * l] = g;
+    // one chunk: the tile epilogue writes g * sum to plane 0 as y
+    mats[2 * l + 1] = dev_mat(kFmtNvfp4Tiled, y.down, nullptr, y.down_scale, s, L.down.nchunks > 1 ? nullptr : part,
+                              D, F, L.down, reinterpret_cast<char*>(part), N, 0);
+  }
+  equal_ranges(L.gate_up.ntiles, L.grid_gate_up, reinterpret_cast<WgRange*>(host.data() + off_rgu));
+  equal_ranges((int64_t)L.down.ntiles * L.down.nchunks, L.grid_down, reinterpret_cast<WgRange*>(host.data() + off_rdn));
+  if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return WQ_ERROR_LAUNCH;
+  plan->workspace = workspace;
+  plan->workspace_bytes = workspace_bytes;
+  plan->h = h;
+  plan->layers = count;
+  plan->D = D;
+  plan->F = F;
+  plan->N = N;
+  plan->grid_gate_up = L.grid_gate_up;
+  plan->grid_down = L.grid_down;
+  plan->down_chunks = L.down.nchunks;
+  plan->reserved = 0;
+  plan->ranges_gate_up_offset = off_rgu;
+  plan->ranges_down_offset = off_rdn;
+  plan->ssp_offset = off_ssp;
+  return WQ_SUCCESS;
+}
+
+wq_status wq_mlp_chain_launch(const wq_mlp_plan* plan, void* stream) {
+  if (!plan || !plan->workspace || !plan->h || plan->layers < 1 || plan->N < 1 || plan->N > 8 ||
+      plan->grid_gate_up < 1 || plan->grid_down < 1 || plan->D < 1 ||
+      plan->ranges_gate_up_offset >= plan->workspace_bytes || plan->ranges_down_offset >= plan->workspace_bytes ||
+      plan->ssp_offset >= plan->workspace_bytes)
+    return WQ_ERROR_INVALID_VALUE;
+  const char* ws = static_cast<const char*>(plan->workspace);
+  const DevMat* mats = reinterpret_cast<const DevMat*>(ws);
+  const WgRange* rgu = reinterpret_cast<const WgRange*>(ws + plan->ranges_gate_up_offset);
+  const WgRange* rdn = reinterpret_cast<const WgRange*>(ws + plan->ranges_down_offset);
+  float* ssp = reinterpret_cast<float*>(static_cast<char*>(plan->workspace) + plan->ssp_offset);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const DevMat none{};
+  const int N = plan->N;
+  hipError_t e = launch_chain_reduce(plan->h, nullptr, plan->D, N, ssp, s);
+  for (int l = 0; l < plan->layers && e == hipSuccess; ++l) {
+    e = launch_stream(N, kModeTiledGlu, mats + 2 * l, rgu, none, plan->grid_gate_up, lds_bytes_for(N) + kArgLdsBytes,
+                      s);
+    if (e == hipSuccess)
+      e = launch_stream(N, kModeTiledWide, mats + 2 * l + 1, rdn, none, plan->grid_down, lds_bytes_for(N), s);
+    if (e == hipSuccess) e = launch_chain_reduce(plan->h, mats + 2 * l + 1, plan->D, N, ssp, s);
+  }
+  return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
 }
 
 }  // extern "C"

@@ -74,6 +74,22 @@ struct DevMat {
   int ntiles;         // ceil(M / 16)
   int64_t unit0;      // index of this matrix's first unit in the pass
   uint64_t* best;     // head acceptance: greedy keys [workgroup][8] (null otherwise)
+  // Gate/up product of a chained MLP layer (kModeTiledGlu) only: rows
+  // 16t..16t+7 of a tile are gate rows 8t..8t+7 (tensor scale g), rows
+  // 16t+8..16t+15 the up rows of the same f (tensor scale g2).  X is not
+  // read from `x`: it is RMSNorm(h) * gamma, rounded to BF16, made while
+  // staging from the residual h [N][K], gamma [K] and the sum-of-squares
+  // partials ssp [N][nparts] of h.  Outputs: s [N][M/2] (BF16), and the
+  // staged X itself, a [N][K] (BF16).
+  const float* h;
+  const float* ssp;
+  const uint16_t* gamma;
+  uint16_t* aout;
+  uint16_t* sout;
+  float g2;
+  float eps;
+  int nparts;
+  int pad;
 };
 
 // First unit (and the matrix holding it) of each workgroup's run.
@@ -126,6 +142,11 @@ constexpr int kModeFp8 = 2;           // FP8-row only
 constexpr int kModeMixed = 3;         // any formats
 constexpr int kModeTiled = 4;         // tiled NVFP4 and tiled FP8-row only
 constexpr int kModeTiledArgmax = 5;   // one tiled matrix, greedy keys per workgroup (head acceptance)
+// Chained MLP layers: few tiles per workgroup, so 16 waves (with a shallower
+// ring, to fit their registers) let every tile of a workgroup stream at once.
+constexpr int kModeTiledGlu = 6;      // tiled NVFP4 gate/up with RMSNorm staging and SwiGLU outputs
+constexpr int kModeTiledWide = 7;     // tiled NVFP4 / FP8 at 16 waves, static ranges only
+constexpr int kPrefetchWide = 3;
 
 template <int MODE>
 __host__ __device__ constexpr int threads_for_mode() {
@@ -135,6 +156,10 @@ constexpr int waves_for_mode(int mode) {
   return ((mode == kModeTiled || mode == kModeTiledArgmax) ? kThreadsTiled : kThreads) / 64;
 }
 
+// Chained-layer residual update: one workgroup of kChainThreads per
+// kChainThreads outputs of one column; also each block's sum of squares.
+constexpr int kChainThreads = 256;
+
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevMat& one, int grid, int N,
@@ -142,6 +167,11 @@ hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevM
 // the tiled verify pass with N read from n_dev (a plan prepared for N = 8)
 hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const int32_t* n_dev, int grid,
                              hipStream_t stream);
+// h[n][m] += the down product of `down` (a device-side descriptor: its
+// chunk partial sums in chunk order, times g; or its y for one chunk),
+// then ssp[n][p] = sum of h[n][m]^2 over block p's outputs.  down == null:
+// ssp only.
+hipError_t launch_chain_reduce(float* h, const DevMat* down, int D, int N, float* ssp, hipStream_t stream);
 hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t* drafts, int32_t* tokens,
                          int32_t* accepted, hipStream_t stream);
 

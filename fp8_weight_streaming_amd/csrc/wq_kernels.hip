@@ -97,6 +97,9 @@ constexpr int kAuxOut = 16;
 __device__ __forceinline__ void bstore4(float v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, kAuxOut);
 }
+__device__ __forceinline__ void bstore2(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, kAuxOut);
+}
 // A buffer offset past every output buffer (outputs are < 2 GiB): the
 // hardware range check drops stores there.
 constexpr uint32_t kDropOffset = 0x80000000u;
@@ -158,6 +161,76 @@ __device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0
       const int p = p0 + j * (int)blockDim.x;
       const int n = p / kc_pad, kc = p - n * kc_pad;
       if (p < total) *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = v[j];
+    }
+  }
+}
+
+// FP32 -> BF16 bits, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- staging of an RMS-normalized X (chained MLP layers) -----------------
+// X[n][k] = BF16(h[n][k] * r[n] * gamma[k]), r[n] = 1 / sqrt(ss[n] / K + eps),
+// with ss[n] the sum of the nparts partial sums of squares of column n
+// (added in order) -- the RMSNorm of a pre-norm transformer layer, computed
+// once per workgroup from the FP32 residual stream instead of by a kernel of
+// its own.  Every workgroup computes the same bits; the pieces of 16 bytes
+// numbered 256j .. 256j + 255 are also written to aout by workgroup
+// j mod gridDim.x, so that the normalized input is visible to the caller.
+// r[n] goes to the 512 bytes past the zero block.  Every thread calls this.
+constexpr int kNormLoads = 4;
+template <int N>
+__device__ void stage_norm(char* lds, const DevMat& mt, int kc_pad) {
+  float* rl = reinterpret_cast<float*>(lds + kZeroOffset<N>() + kZeroBytes<N>());
+  const int K = mt.K;
+  if (threadIdx.x < N) {
+    const float* sp = mt.ssp + (size_t)threadIdx.x * mt.nparts;
+    float ss = 0.0f;
+    for (int p = 0; p < mt.nparts; ++p) ss += sp[p];
+    rl[threadIdx.x] = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(ss, (float)K) + mt.eps));
+  }
+  __syncthreads();
+  const int valid = K / 8;
+  const int total = kc_pad * N;
+  for (int p0 = threadIdx.x; p0 < total; p0 += kNormLoads * (int)blockDim.x) {
+    f32x4 h0[kNormLoads], h1[kNormLoads];
+    u32x4 gm[kNormLoads];
+#pragma unroll
+    for (int j = 0; j < kNormLoads; ++j) {
+      const int p = p0 + j * (int)blockDim.x;
+      const int n = p / kc_pad, kc = p - n * kc_pad;
+      h0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      h1[j] = h0[j];
+      gm[j] = u32x4{0u, 0u, 0u, 0u};
+      if (p < total && kc < valid) {
+        const float* hp = mt.h + (size_t)n * K + 8 * kc;
+        h0[j] = *reinterpret_cast<const f32x4*>(hp);
+        h1[j] = *reinterpret_cast<const f32x4*>(hp + 4);
+        gm[j] = *reinterpret_cast<const u32x4*>(mt.gamma + 8 * kc);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kNormLoads; ++j) {
+      const int p = p0 + j * (int)blockDim.x;
+      if (p >= total) continue;
+      const int n = p / kc_pad, kc = p - n * kc_pad;
+      const float r = rl[n];
+      const float hv[8] = {h0[j].x, h0[j].y, h0[j].z, h0[j].w, h1[j].x, h1[j].y, h1[j].z, h1[j].w};
+      u32x4 o = {0u, 0u, 0u, 0u};
+      if (kc < valid) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float glo = __uint_as_float(gm[j][i] << 16), ghi = __uint_as_float(gm[j][i] & 0xFFFF0000u);
+          const float lo = (hv[2 * i] * r) * glo, hi = (hv[2 * i + 1] * r) * ghi;
+          o[i] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+        }
+        if (((p >> 8) % (int)gridDim.x) == (int)blockIdx.x)
+          *reinterpret_cast<u32x4*>(mt.aout + (size_t)n * K + 8 * kc) = o;
+      }
+      *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = o;
     }
   }
 }
@@ -331,13 +404,21 @@ __device__ __forceinline__ uint64_t greedy_key(float v, int m) {
   return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)m);
 }
 
-// ARG: also keep, per lane and register r, the greedy key of the lane's
-// outputs (lanes 0..31: column 4 * (lane / 16) + r, rows 16 t + lane % 16).
+// What a finished tile does with its sums (EPI):
+//  kEpiStore   store y (or the chunk's partial sums), paired as below;
+//  kEpiArgmax  the same, and keep, per lane and register r, the greedy key
+//              of the lane's outputs (lanes 0..31: column 4 * (lane / 16) + r,
+//              rows 16 t + lane % 16);
+//  kEpiGlu     gate/up tiles (rows c < 8 gate, c >= 8 up of f = 8 t + c % 8):
+//              store s[n][f] = BF16(silu(gate) * up), silu(v) = v / (1 + e^-v).
 //
 // stage() stages the run's X into LDS between two workgroup barriers.  The
 // run calls it once on every path, after issuing its first PF steps of
 // weight loads, so that their round trip overlaps the staging.
-template <int N, int PF, bool FP8, bool ARG, typename Stage>
+constexpr int kEpiStore = 0;
+constexpr int kEpiArgmax = 1;
+constexpr int kEpiGlu = 2;
+template <int N, int PF, bool FP8, int EPI, typename Stage>
 __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds,
                           uint64_t* bestk, Stage&& stage) {
   if (first >= end) {
@@ -441,7 +522,11 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
   const bool split = mt.nchunks > 1;
   float* const obase = split ? mt.part + (size_t)chunk * N * mt.M : mt.y;
   // (no output buffer -- head acceptance without logits -- drops every store)
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc_uniform(obase, obase ? (uint64_t)N * (uint64_t)mt.M * 4u : 0u);
+  const int F = mt.M / 2;  // kEpiGlu: outputs per column
+  const __amdgpu_buffer_rsrc_t ro =
+      EPI == kEpiGlu ? make_rsrc_uniform(mt.sout, (uint64_t)N * (uint64_t)F * 2u)
+                     : make_rsrc_uniform(obase, obase ? (uint64_t)N * (uint64_t)mt.M * 4u : 0u);
+  uint32_t sbits[4] = {0u, 0u, 0u, 0u};  // kEpiGlu: BF16 outputs
   const float gscale = split ? 1.0f : mt.g;
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
   float prev[4] = {0.f, 0.f, 0.f, 0.f};
@@ -459,7 +544,23 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       half(c1[slot], sw[slot].y, xo + 256u * N);
     }
     const bool fin = cst == nst - 1;
-    if (fin) {
+    if (fin && EPI == kEpiGlu) {
+      // sums sit at lane 16 * (n / 4) + c (and again 32 lanes up); the gate
+      // row c < 8 and the up row c + 8 of one f are 8 lanes apart
+      const float gs = c < 8 ? mt.g : mt.g2;
+      const int f = 8 * (tile0 + ci) + (c & 7);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
+        const float v = gs * (__uint_as_float(p.x) + __uint_as_float(p.y));
+        acc[r] = 0.f;
+        const float up = __shfl_xor(v, 8);
+        const int n = r + 4 * ((lane >> 4) & 1);
+        const bool live = lane < 32 && c < 8 && n < N && f < F;
+        so[r] = live ? (uint32_t)((n * F + f) * 2) : kDropOffset;
+        sbits[r] = bf16_rne(__fdiv_rn(v, 1.0f + expf(-v)) * up);
+      }
+    } else if (fin) {
       const int t = tile0 + ci;
       const bool odd = (t & 1) != 0;
       // emit a pair (odd tile), or a lone even tile at the end of the share
@@ -488,7 +589,7 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
                                                          false, false);
         sum[r] = __uint_as_float(lane < 32 ? q.x : q.y);
         prev[r] = cur;
-        if constexpr (ARG) {
+        if constexpr (EPI == kEpiArgmax) {
           const int mo = (tile0 + ci) * 16 + c;  // the lane's own row
           const bool own = lane < 32 && mo < mt.M && 4 * (lane >> 4) + r < N;
           const uint64_t key = own ? greedy_key(cur, mo) : 0ull;
@@ -500,7 +601,12 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       }
     }
 #pragma unroll
-    for (int r = 0; r < kStores; ++r) bstore4(sum[r], ro, fin ? so[r] : kDropOffset);
+    for (int r = 0; r < kStores; ++r) {
+      if constexpr (EPI == kEpiGlu)
+        bstore2(sbits[r], ro, fin ? so[r] : kDropOffset);
+      else
+        bstore4(sum[r], ro, fin ? so[r] : kDropOffset);
+    }
     if (++cst == nst) { cst = 0; ++ci; }
   };
 
@@ -513,7 +619,12 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
 #pragma unroll
-    for (int r = 0; r < kStores; ++r) bstore4(0.0f, ro, kDropOffset + 4u * (4 * i + r));
+    for (int r = 0; r < kStores; ++r) {
+      if constexpr (EPI == kEpiGlu)
+        bstore2(0u, ro, kDropOffset + 4u * (4 * i + r));
+      else
+        bstore4(0.0f, ro, kDropOffset + 4u * (4 * i + r));
+    }
     load_next(i);
   }
   stage();
@@ -662,14 +773,26 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     const int64_t share0 = u + len * wave / nwaves, share1 = u + len * (wave + 1) / nwaves;
     if constexpr (MODE == kModeTiled) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchTiled, true, false>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
       else
-        tiled_run<N, kPrefetchTiled, false, false>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
     } else if constexpr (MODE == kModeTiledArgmax) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchTiled, true, true>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, true, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, stage);
       else
-        tiled_run<N, kPrefetchTiled, false, true>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, false, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, stage);
+    } else if constexpr (MODE == kModeTiledGlu) {
+      auto stage_norm_x = [&]() {
+        __syncthreads();
+        stage_norm<N>(lds, mt, kc_pad);
+        __syncthreads();
+      };
+      tiled_run<N, kPrefetchWide, false, kEpiGlu>(mt, chunk, share0, share1, lds, bestk, stage_norm_x);
+    } else if constexpr (MODE == kModeTiledWide) {
+      if (mt.fmt == kFmtFp8RowTiled)
+        tiled_run<N, kPrefetchWide, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
+      else
+        tiled_run<N, kPrefetchWide, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
     } else {
       // (written out rather than through stage(): a by-reference lambda on
       // this path kept the descriptor out of scalar registers and made the
@@ -679,9 +802,9 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       __syncthreads();
       auto staged = []() {};
       if (MODE == kModeMixed && mt.fmt == kFmtNvfp4Tiled) {
-        tiled_run<N, 1, false, false>(mt, chunk, share0, share1, lds, bestk, staged);
+        tiled_run<N, 1, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged);
       } else if (MODE == kModeMixed && mt.fmt == kFmtFp8RowTiled) {
-        tiled_run<N, 1, true, false>(mt, chunk, share0, share1, lds, bestk, staged);
+        tiled_run<N, 1, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged);
       } else {
         for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
           const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
@@ -790,6 +913,56 @@ __global__ __launch_bounds__(kThreadsTiled) void stream_kernel_dyn(const DevMat*
     case 7: dyn_body<7>(mats, ranges, lds); break;
     default: dyn_body<8>(mats, ranges, lds); break;
   }
+}
+
+// ---- residual update of a chained MLP layer ---------------------------------
+// Block (p, n) owns outputs m = kChainThreads p + i of column n:
+//   h[n][m] += g * (part[0][n][m] + part[1][n][m] + ...)   (chunk order)
+// for a down product split in K (one chunk: its y, already scaled, is
+// added), and writes the sum of their squares (after the update) to
+// ssp[n][p], the partials from which the next layer's RMSNorm takes its
+// scale (summed in p order).  With no descriptor it only writes ssp.  The
+// sum over a block is a fixed tree (butterfly within a wave, then the waves
+// in order), so every run gives the same bits.
+__global__ __launch_bounds__(kChainThreads) void chain_reduce_kernel(float* __restrict__ h,
+                                                                     const DevMat* __restrict__ down, int D, int N,
+                                                                     float* __restrict__ ssp) {
+  const int n = blockIdx.y, p = blockIdx.x;
+  const int m = p * kChainThreads + (int)threadIdx.x;
+  float v = 0.0f;
+  if (m < D) {
+    const size_t o = (size_t)n * D + m;
+    v = h[o];
+    if (down) {
+      const int nchunks = down->nchunks;
+      float acc = 0.0f;
+      if (nchunks > 1) {
+        for (int c = 0; c < nchunks; ++c) acc += down->part[(size_t)c * N * D + o];
+        acc = down->g * acc;
+      } else {
+        acc = down->y[o];
+      }
+      v = v + acc;
+      h[o] = v;
+    }
+  }
+  float sq = v * v;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+  __shared__ float wsum[kChainThreads / 64];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = sq;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+    for (int w = 0; w < kChainThreads / 64; ++w) t += wsum[w];
+    ssp[(size_t)n * gridDim.x + p] = t;
+  }
+}
+
+hipError_t launch_chain_reduce(float* h, const DevMat* down, int D, int N, float* ssp, hipStream_t stream) {
+  const int parts = (D + kChainThreads - 1) / kChainThreads;
+  hipLaunchKernelGGL(chain_reduce_kernel, dim3(parts, N), dim3(kChainThreads), 0, stream, h, down, D, N, ssp);
+  return hipGetLastError();
 }
 
 // ---- split-K reduction -----------------------------------------------------
@@ -920,6 +1093,8 @@ static hipError_t launch_n(int mode, const DevMat* mats, const WgRange* ranges, 
     case kModeMixed: return launch_nm<N, kModeMixed>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeTiled: return launch_nm<N, kModeTiled>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeTiledArgmax: return launch_nm<N, kModeTiledArgmax>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeTiledGlu: return launch_nm<N, kModeTiledGlu>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeTiledWide: return launch_nm<N, kModeTiledWide>(mats, ranges, one, grid, lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -23,6 +23,11 @@
 //   bytes [1024h + 16l, +16), h = 0..1, lane l = c + 16g: plain bytes
 //     [128s + 64h + 16g, +16) of row 16t + c.
 // The row scales stay a separate FP32 array.
+//
+// Gate/up layout of a chained MLP layer (wq_nvfp4_tile_glu): the tiled NVFP4
+// layout of a 2F-row matrix whose tile t holds gate rows 8t..8t+7 in rows
+// 0..7 and up rows 8t..8t+7 in rows 8..15, so that each tile's epilogue
+// finds both inputs of the gated unit for the same eight outputs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,9 +39,13 @@ namespace {
 
 constexpr int kTileThreads = 256;
 
-// One thread per (tile, step, lane): 32 code bytes and 8 scale bytes.
+// One thread per (tile, step, lane): 32 code bytes and 8 scale bytes.  With
+// codes1 set, M = 2F rows are interleaved from two F-row matrices (codes,
+// scales: gate; codes1, scales1: up) as described above.
 __global__ __launch_bounds__(kTileThreads) void tile_kernel(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ scales, int M, int K,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const uint8_t* __restrict__ codes1,
+                                                            const uint8_t* __restrict__ scales1, int M, int K,
                                                             uint8_t* __restrict__ tiled, int64_t slots) {
   const int64_t id = (int64_t)blockIdx.x * kTileThreads + threadIdx.x;
   if (id >= slots) return;
@@ -46,7 +55,16 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const uint8_t* __res
   const int s = (int)(ts % S);
   const int64_t t = ts / S;
   const int c = l & 15, g = l >> 4;
-  const int64_t row = t * kTileRows + c;
+  int64_t row = t * kTileRows + c;
+  int64_t rows = M;
+  if (codes1) {
+    row = t * (kTileRows / 2) + (c & 7);
+    rows = M / 2;
+    if (c >= 8) {
+      codes = codes1;
+      scales = scales1;
+    }
+  }
   const int64_t rowb = K / 2, srowb = K / 16;
   uint8_t* blk = tiled + ts * kTileBlockBytes;
   for (int h = 0; h < 2; ++h) {
@@ -54,7 +72,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const uint8_t* __res
     for (int j = 0; j < 4; ++j) {
       const int64_t b0 = (int64_t)128 * s + 64 * h + 16 * j + 4 * g;  // first code byte in the row
       uint32_t v = 0;
-      if (row < M && b0 < rowb) v = *reinterpret_cast<const uint32_t*>(codes + row * rowb + b0);
+      if (row < rows && b0 < rowb) v = *reinterpret_cast<const uint32_t*>(codes + row * rowb + b0);
       w[j] = v;
     }
     *reinterpret_cast<uint4*>(blk + 1024 * h + 16 * l) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -66,7 +84,7 @@ __global__ __launch_bounds__(kTileThreads) void tile_kernel(const uint8_t* __res
     for (int h = 0; h < 2; ++h)
       for (int j = 0; j < 4; ++j) {
         const int64_t col = (int64_t)16 * s + 8 * h + 2 * j + p;
-        const uint32_t b = (row < M && col < srowb) ? scales[row * srowb + col] : 0u;
+        const uint32_t b = (row < rows && col < srowb) ? scales[row * srowb + col] : 0u;
         sv[h] |= b << (8 * j);
       }
     *reinterpret_cast<uint2*>(blk + kTileCodeBytes + 8 * (16 * p + c)) = make_uint2(sv[0], sv[1]);
@@ -182,7 +200,22 @@ wq_status wq_nvfp4_tile(const uint8_t* codes, const uint8_t* scales, int M, int 
   const int64_t slots = wq::tile_slots(M, K);
   const int grid = (int)((slots + wq::kTileThreads - 1) / wq::kTileThreads);
   hipLaunchKernelGGL(wq::tile_kernel, dim3(grid), dim3(wq::kTileThreads), 0, static_cast<hipStream_t>(stream), codes,
-                     scales, M, K, tiled, slots);
+                     scales, nullptr, nullptr, M, K, tiled, slots);
+  return hipGetLastError() == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+wq_status wq_nvfp4_tile_glu(const uint8_t* gate_codes, const uint8_t* gate_scales, const uint8_t* up_codes,
+                            const uint8_t* up_scales, int F, int K, uint8_t* tiled, void* stream) {
+  if (!gate_codes || !gate_scales || !up_codes || !up_scales || !tiled) return WQ_ERROR_INVALID_VALUE;
+  if (F < 1 || K < 1) return WQ_ERROR_INVALID_VALUE;
+  if (F % 8 != 0 || F > (1 << 29) || !wq::shape_ok(2 * F, K)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  if (((uintptr_t)gate_codes & 15u) || ((uintptr_t)gate_scales & 15u) || ((uintptr_t)up_codes & 15u) ||
+      ((uintptr_t)up_scales & 15u) || ((uintptr_t)tiled & 15u))
+    return WQ_ERROR_MISALIGNED;
+  const int64_t slots = wq::tile_slots(2 * F, K);
+  const int grid = (int)((slots + wq::kTileThreads - 1) / wq::kTileThreads);
+  hipLaunchKernelGGL(wq::tile_kernel, dim3(grid), dim3(wq::kTileThreads), 0, static_cast<hipStream_t>(stream),
+                     gate_codes, gate_scales, up_codes, up_scales, 2 * F, K, tiled, slots);
   return hipGetLastError() == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
 }
 

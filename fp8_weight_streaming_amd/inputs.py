@@ -200,7 +200,7 @@ class MlpLayerInputs:
     gamma: np.ndarray   # uint16 [D] BF16 norm weights
 
 
-def mlp_layer_inputs(D: int, F: int, seed: int, down_gain: float = 0.25) -> MlpLayerInputs:
+def mlp_layer_inputs(D: int, F: int, seed: int, down_gain: float = 0.25, up_gain: float = 1.0) -> MlpLayerInputs:
     """Weights of one MLP layer.  Tensor scales put the gate/up outputs near
     unit size for unit-size normalized inputs, and scale each layer's
     addition to the residual by about down_gain, so that a stack of many
@@ -208,7 +208,7 @@ def mlp_layer_inputs(D: int, F: int, seed: int, down_gain: float = 0.25) -> MlpL
     g_gu = float(np.float32(1.0 / (NVFP4_DRAW_RMS * np.sqrt(D))))
     g_d = float(np.float32(down_gain / (NVFP4_DRAW_RMS * np.sqrt(F))))
     gate = nvfp4_inputs(F, D, 1, 4 * seed + 0, g_gu)
-    up = nvfp4_inputs(F, D, 1, 4 * seed + 1, g_gu)
+    up = nvfp4_inputs(F, D, 1, 4 * seed + 1, float(np.float32(g_gu * up_gain)))
     down = nvfp4_inputs(D, F, 1, 4 * seed + 2, g_d)
     rng = _rng(4 * seed + 3)
     gamma = to_bf16((1.0 + 0.2 * rng.standard_normal(D)).astype(np.float32))

@@ -58,6 +58,20 @@ class WqVerifyPlan(ctypes.Structure):
                 ("reduce_runs", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class WqMlpLayer(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("gate_scale", ctypes.c_float), ("up_scale", ctypes.c_float), ("down_scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+class WqMlpPlan(ctypes.Structure):
+    _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("h", ctypes.c_void_p),
+                ("layers", ctypes.c_int32), ("D", ctypes.c_int32), ("F", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("grid_gate_up", ctypes.c_int32), ("grid_down", ctypes.c_int32), ("down_chunks", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("ranges_gate_up_offset", ctypes.c_size_t),
+                ("ranges_down_offset", ctypes.c_size_t), ("ssp_offset", ctypes.c_size_t)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _S = ctypes.c_size_t
@@ -114,11 +128,23 @@ _lib.wq_verify_launch_n.restype = _I
 _lib.wq_verify_launch_n.argtypes = [ctypes.POINTER(WqVerifyPlan), _P, _P]
 _lib.wq_gemm_fp8row_tiled.restype = _I
 _lib.wq_gemm_fp8row_tiled.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _S, _P]
+_lib.wq_nvfp4_tile_glu.restype = _I
+_lib.wq_nvfp4_tile_glu.argtypes = [_P, _P, _P, _P, _I, _I, _P, _P]
+_lib.wq_mlp_chain_workspace_bytes.restype = _S
+_lib.wq_mlp_chain_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.wq_mlp_chain_split.restype = _I
+_lib.wq_mlp_chain_split.argtypes = [_I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.wq_mlp_chain_prepare.restype = _I
+_lib.wq_mlp_chain_prepare.argtypes = [ctypes.POINTER(WqMlpLayer), _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P,
+                                      _S, _P, ctypes.POINTER(WqMlpPlan)]
+_lib.wq_mlp_chain_launch.restype = _I
+_lib.wq_mlp_chain_launch.argtypes = [ctypes.POINTER(WqMlpPlan), _P]
 
 EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
             "wq_head_accept_workspace_bytes", "wq_head_accept", "wq_quantize_fp8row", "wq_quantize_nvfp4",
-            "wq_verify_launch_n",
+            "wq_verify_launch_n", "wq_nvfp4_tile_glu", "wq_mlp_chain_workspace_bytes", "wq_mlp_chain_split",
+            "wq_mlp_chain_prepare", "wq_mlp_chain_launch",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
@@ -375,3 +401,52 @@ def wq_verify_launch_n(plan: WqVerifyPlan, n_device, stream=None):
     """Launch a plan prepared for N = 8 with the column count read from the
     int32 device tensor n_device when the kernels run."""
     _check(_lib.wq_verify_launch_n(ctypes.byref(plan), _ptr(n_device), _stream(stream)), "wq_verify_launch_n")
+
+
+def wq_nvfp4_tile_glu(gate_codes, gate_scales, up_codes, up_scales, tiled, stream=None,
+                      F: Optional[int] = None, D: Optional[int] = None):
+    """Interleave gate/up NVFP4 weights [F][D] into the chain's tiled layout."""
+    if F is None:
+        F = gate_codes.shape[0]
+    if D is None:
+        D = 2 * gate_codes.shape[1]
+    _check(_lib.wq_nvfp4_tile_glu(_ptr(gate_codes), _ptr(gate_scales), _ptr(up_codes), _ptr(up_scales), F, D,
+                                  _ptr(tiled), _stream(stream)), "wq_nvfp4_tile_glu")
+
+
+class MlpLayer:
+    """One chained layer's device buffers (tensors or raw pointers)."""
+
+    def __init__(self, gate_up, down, gamma, gate_scale: float, up_scale: float, down_scale: float):
+        self.gate_up, self.down, self.gamma = gate_up, down, gamma
+        self.gate_scale, self.up_scale, self.down_scale = gate_scale, up_scale, down_scale
+
+
+def wq_mlp_chain_workspace_bytes(layers: int, D: int, F: int, N: int) -> int:
+    return int(_lib.wq_mlp_chain_workspace_bytes(layers, D, F, N))
+
+
+def wq_mlp_chain_split(D: int, F: int):
+    kc, nc = _I(0), _I(0)
+    _check(_lib.wq_mlp_chain_split(D, F, ctypes.byref(kc), ctypes.byref(nc)), "wq_mlp_chain_split")
+    return kc.value, nc.value
+
+
+def wq_mlp_chain_prepare(layers: Sequence[MlpLayer], D: int, F: int, N: int, eps: float, h, a, s, workspace,
+                         stream=None, workspace_bytes: Optional[int] = None) -> WqMlpPlan:
+    """Write the chain's device table into `workspace`; returns the plan."""
+    arr = (WqMlpLayer * max(1, len(layers)))()
+    for i, y in enumerate(layers):
+        arr[i] = WqMlpLayer(_ptr(y.gate_up), _ptr(y.down), _ptr(y.gamma), float(y.gate_scale), float(y.up_scale),
+                            float(y.down_scale), 0)
+    plan = WqMlpPlan()
+    wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
+    _check(_lib.wq_mlp_chain_prepare(arr, len(layers), D, F, N, float(eps), _ptr(h), _ptr(a), _ptr(s),
+                                     _ptr(workspace), wsb, _stream(stream), ctypes.byref(plan)),
+           "wq_mlp_chain_prepare")
+    return plan
+
+
+def wq_mlp_chain_launch(plan: WqMlpPlan, stream=None):
+    """Run the prepared layers (launches only); updates h in place."""
+    _check(_lib.wq_mlp_chain_launch(ctypes.byref(plan), _stream(stream)), "wq_mlp_chain_launch")

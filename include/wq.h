@@ -292,6 +292,80 @@ wq_status wq_quantize_fp8row(const uint16_t* w, int M, int K, uint8_t* q, float*
 wq_status wq_quantize_nvfp4(const uint16_t* w, int M, int K, float global_scale,
                             uint8_t* codes, uint8_t* scales, void* stream);
 
+/* Chained MLP layers over the verify columns.  The crit-hub engine card
+ * "mtp7-device-confidence" (section "Limits") traces its short-prompt
+ * latency to the many small kernels each layer launches, and (section
+ * "Design", row "Decode") runs a decode round as one device graph; the
+ * pages give no layer equations, so the layer is a pre-norm dense MLP block
+ * on the N columns of an FP32 residual stream h [N][D]:
+ *     r[n] = 1 / sqrt(sum_k h[n][k]^2 / D + eps)
+ *     a    = BF16(h * r * gamma)                (gamma: BF16 [D])
+ *     s    = BF16(silu(a . Wg^T) * (a . Wu^T))  (Wg, Wu: NVFP4 [F][D])
+ *     h   += s . Wd^T                           (Wd: NVFP4 [D][F])
+ * with silu(v) = v / (1 + e^-v), BF16 rounding to nearest-even, and FP32
+ * sums as in the GEMM calls.  Layers run in order, three kernels each
+ * (gate/up with the RMSNorm made while staging its input and SwiGLU in its
+ * epilogue; down, split in K; the residual update, which also makes the
+ * next layer's sums of squares) plus one small kernel in front: no host
+ * work between layers, and capture-safe once prepared.
+ *
+ * wq_nvfp4_tile_glu: the gate/up weights in the interleaved tiled layout
+ *   the chain reads (tile t = gate rows 8t..8t+7 then up rows 8t..8t+7);
+ *   gate/up codes [F][D/2] and scales [F][D/16] as wq_gemm_nvfp4 takes
+ *   them, F % 8 == 0, D % 32 == 0; `tiled` holds wq_nvfp4_tiled_bytes(2F, D)
+ *   bytes.  The down weights use wq_nvfp4_tile (M = D, K = F).
+ * wq_mlp_layer: one layer's device buffers (HOST array of them).
+ * wq_mlp_chain_prepare: checks the shapes (N 1..8, D % 32 == 0 and
+ *   D <= 8704, F % 32 == 0, eps finite >= 0, all pointers non-null and
+ *   16-byte aligned) and writes the descriptor table into `workspace`
+ *   (>= wq_mlp_chain_workspace_bytes(layers, D, F, N) bytes, 16-byte
+ *   aligned; one asynchronous host-to-device copy on `stream`), filling
+ *   `plan`.  h [N][D] FP32 (in/out), a [N][D] and s [N][F] (BF16 outputs:
+ *   the last layer's normalized input and gated product) are device
+ *   buffers that must not overlap each other, the workspace or a weight.
+ * wq_mlp_chain_launch: runs the layers (launch only; any number of times,
+ *   on a stream ordered after the prepare's copy, while every buffer stays
+ *   alive).  Each run updates h in place.  Results are deterministic, and
+ *   running the layers in one call or one layer per call gives the same
+ *   bits.  An all-zero column with eps = 0 gives NaN (0 * inf), as the
+ *   formula does. */
+typedef struct wq_mlp_layer {
+  const void* gate_up;    /* from wq_nvfp4_tile_glu */
+  const void* down;       /* from wq_nvfp4_tile, D x F */
+  const uint16_t* gamma;  /* BF16 [D] */
+  float gate_scale;       /* tensor scales of Wg, Wu, Wd */
+  float up_scale;
+  float down_scale;
+  int32_t reserved;
+} wq_mlp_layer;
+
+typedef struct wq_mlp_plan {
+  void* workspace;
+  size_t workspace_bytes;
+  float* h;
+  int32_t layers;
+  int32_t D;
+  int32_t F;
+  int32_t N;
+  int32_t grid_gate_up;
+  int32_t grid_down;
+  int32_t down_chunks;
+  int32_t reserved;
+  size_t ranges_gate_up_offset;
+  size_t ranges_down_offset;
+  size_t ssp_offset;
+} wq_mlp_plan;
+
+wq_status wq_nvfp4_tile_glu(const uint8_t* gate_codes, const uint8_t* gate_scales, const uint8_t* up_codes,
+                            const uint8_t* up_scales, int F, int D, uint8_t* tiled, void* stream);
+size_t wq_mlp_chain_workspace_bytes(int layers, int D, int F, int N);
+/* How the chain splits the down product's K = F: chunk length and count. */
+wq_status wq_mlp_chain_split(int D, int F, int* k_chunk, int* n_chunks);
+wq_status wq_mlp_chain_prepare(const wq_mlp_layer* layers, int count, int D, int F, int N, float eps,
+                               float* h, uint16_t* a, uint16_t* s, void* workspace, size_t workspace_bytes,
+                               void* stream, wq_mlp_plan* plan);
+wq_status wq_mlp_chain_launch(const wq_mlp_plan* plan, void* stream);
+
 /* Measurement kernels (not part of the product; they price it).  The crit
  * README's Eval turns the GPU's measured bandwidth into a floor for each
  * kernel, and the NInfer README ships a standalone bandwidth probe; these

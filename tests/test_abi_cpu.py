@@ -186,3 +186,47 @@ def test_device_n_launch_argument_errors(wq):
     assert lib.wq_verify_launch_n(C.byref(plan), FAKE, 0) == 1         # plan not prepared for N = 8
     plan.N, plan.mode = 8, 3
     assert lib.wq_verify_launch_n(C.byref(plan), FAKE, 0) == 1         # not an all-tiled plan
+
+
+def test_chain_argument_errors(wq):
+    import ctypes as C
+    lib = wq.lib()
+    INV, SHAPE, MIS, WS, DEVERR = 1, 2, 3, 4, 6
+    layer = wq.WqMlpLayer(FAKE, FAKE, FAKE, 1.0, 1.0, 1.0, 0)
+    arr = (wq.WqMlpLayer * 2)(layer, layer)
+    plan = wq.WqMlpPlan()
+
+    def prep(count=2, D=256, F=512, N=4, eps=1e-6, h=FAKE, a=FAKE, s=FAKE, ws=FAKE, wsb=1 << 30, layers=arr,
+             p=C.byref(plan)):
+        return lib.wq_mlp_chain_prepare(layers, count, D, F, N, eps, h, a, s, ws, wsb, 0, p)
+
+    assert prep(p=None) == INV and prep(layers=None) == INV
+    assert prep(count=0) == INV and prep(N=0) == INV and prep(N=9) == INV
+    assert prep(D=48) == SHAPE and prep(F=40) == SHAPE and prep(D=8736) == SHAPE      # D past one LDS chunk
+    assert prep(eps=-1.0) == INV and prep(eps=float("inf")) == INV and prep(eps=float("nan")) == INV
+    assert prep(h=0) == INV and prep(a=0) == INV and prep(s=0) == INV
+    assert prep(h=MISALIGNED) == MIS and prep(s=FAKE + 2) == MIS
+    bad = (wq.WqMlpLayer * 2)(layer, wq.WqMlpLayer(FAKE, 0, FAKE, 1.0, 1.0, 1.0, 0))
+    assert prep(layers=bad) == INV
+    bad = (wq.WqMlpLayer * 2)(layer, wq.WqMlpLayer(FAKE, FAKE, FAKE + 2, 1.0, 1.0, 1.0, 0))
+    assert prep(layers=bad) == MIS
+    assert prep(ws=0) == WS and prep(ws=MISALIGNED) == MIS
+    assert prep() == DEVERR if not _has_gpu() else True                 # valid arguments reach the device query
+    assert lib.wq_mlp_chain_workspace_bytes(0, 256, 512, 4) == 0 and lib.wq_mlp_chain_workspace_bytes(1, 40, 512, 4) == 0
+    kc, nc = C.c_int(0), C.c_int(0)
+    assert lib.wq_mlp_chain_split(256, 40, C.byref(kc), C.byref(nc)) == SHAPE
+    assert lib.wq_mlp_chain_split(256, 512, None, C.byref(nc)) == INV
+    assert lib.wq_mlp_chain_launch(None, 0) == INV
+    assert lib.wq_mlp_chain_launch(C.byref(wq.WqMlpPlan()), 0) == INV                    # never prepared
+    tg = lib.wq_nvfp4_tile_glu
+    assert tg(0, FAKE, FAKE, FAKE, 64, 256, FAKE, 0) == INV and tg(FAKE, FAKE, FAKE, FAKE, 0, 256, FAKE, 0) == INV
+    assert tg(FAKE, FAKE, FAKE, FAKE, 60, 256, FAKE, 0) == SHAPE and tg(FAKE, FAKE, FAKE, FAKE, 64, 48, FAKE, 0) == SHAPE
+    assert tg(FAKE, FAKE, FAKE + 4, FAKE, 64, 256, FAKE, 0) == MIS
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
