@@ -474,6 +474,120 @@ def device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n, reps=9):
     return out
 
 
+def chain_bytes(D, F, N, layers):
+    """Bytes a chained MLP pass must move: per layer the NVFP4 gate, up and
+    down weights (0.5625 B each), gamma (2D), the residual read and written
+    (4ND each), the normalized input written (2ND), the gated product
+    written and read (2NF each) and three tensor scales."""
+    per = 3 * D * F // 2 + 3 * D * F // 16 + 2 * D + 8 * N * D + 2 * N * D + 4 * N * F + 12
+    return per * layers
+
+
+def chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=48, reps=5):
+    """The verify pass as chained MLP layers (wq_mlp_chain_*): each of the
+    pass's layers applies RMSNorm, gate/up (rows 0..F-1 and F..2F-1 of its
+    gate_up matrix), SwiGLU and down to the residual stream of the N verify
+    columns, three kernels per layer, eager and replayed as one HIP graph.
+    Layer 0 is checked against the oracle on sampled outputs."""
+    import oracle
+    from oracle import chain
+    dev = torch.device("cuda:0")
+    layers = len(wl.matrices) // 4
+    D, F = wl.matrices[3].M, wl.matrices[3].K
+    rng = np.random.default_rng(2024)
+    descs, keep = [], []
+    for l in range(layers):
+        c, sc = mats_dev[4 * l + 2][0], mats_dev[4 * l + 2][1]
+        gu = torch.empty(wq.wq_nvfp4_tiled_bytes(2 * F, D), dtype=torch.uint8, device=dev)
+        wq.wq_nvfp4_tile_glu(c[:F], sc[:F], c[F:], sc[F:], gu, stream)
+        gamma = torch.from_numpy(inputs.to_bf16((1 + 0.2 * rng.standard_normal(D)).astype(np.float32))
+                                 .view(np.int16)).to(dev)
+        keep.append((gu, gamma))
+        descs.append(wq.MlpLayer(gu, mats_dev[4 * l + 3][4], gamma, wl.g, wl.g, wl.g))
+    torch.cuda.synchronize()
+    eps = 1e-6
+    h0_host = inputs.residual_inputs(NMAX, D, seed=2025)
+    rows = {}
+    for N in (1, 2, 4, 8):
+        h0 = torch.from_numpy(h0_host[:N].copy()).to(dev)
+        h = h0.clone()
+        a = torch.zeros((N, D), dtype=torch.int16, device=dev)
+        sb = torch.zeros((N, F), dtype=torch.int16, device=dev)
+        ws = torch.empty(wq.wq_mlp_chain_workspace_bytes(layers, D, F, N), dtype=torch.uint8, device=dev)
+        plan = wq.wq_mlp_chain_prepare(descs, D, F, N, eps, h, a, sb, ws, stream)
+        for _ in range(2):
+            wq.wq_mlp_chain_launch(plan, stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            h.copy_(h0)
+            e0.record(stream)
+            wq.wq_mlp_chain_launch(plan, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=side):
+            wq.wq_mlp_chain_launch(plan, side)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            h.copy_(h0)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
+        nb = chain_bytes(D, F, N, layers)
+        kc, nc = wq.wq_mlp_chain_split(D, F)
+        rows[str(N)] = {"eager_us": eager_us, "graph_us": graph_us, "us_per_layer_graph": graph_us / layers,
+                        "algorithmic_bytes": nb, "gbps_graph": nb / graph_us / 1e3,
+                        "pct_of_8TBps_graph": 100 * nb / graph_us / 1e3 / PEAK_GBPS,
+                        "pct_of_8TBps_eager": 100 * nb / eager_us / 1e3 / PEAK_GBPS,
+                        "launches": 3 * layers + 1, "down_k_chunks": nc}
+        del graph, ws, plan
+
+    # layer 0 at N = 8 against the oracle (sampled rows of s and h)
+    N = 8
+    h0 = torch.from_numpy(h0_host.copy()).to(dev)
+    h = h0.clone()
+    a = torch.zeros((N, D), dtype=torch.int16, device=dev)
+    sb = torch.zeros((N, F), dtype=torch.int16, device=dev)
+    ws = torch.empty(wq.wq_mlp_chain_workspace_bytes(1, D, F, N), dtype=torch.uint8, device=dev)
+    plan = wq.wq_mlp_chain_prepare(descs[:1], D, F, N, eps, h, a, sb, ws, stream)
+    wq.wq_mlp_chain_launch(plan, stream)
+    torch.cuda.synchronize()
+    a_bits = a.cpu().numpy().view(np.uint16)
+    s_bits = sb.cpu().numpy().view(np.uint16)
+    h1 = h.cpu().numpy().astype(np.float64)
+    gamma0 = keep[0][1].cpu().numpy().view(np.uint16)
+    a_ref = chain.normalize(h0_host.astype(np.float64), gamma0, eps)
+    a_gpu = chain.bf16_value(a_bits)
+    ok = bool(np.all(np.abs(a_gpu - a_ref) <= 2.0 ** -7 * np.abs(a_ref)))
+    gu, dn = host[2], host[3]
+    f = np.unique(np.concatenate([rng.integers(0, F, check_rows), [0, F - 1]]))
+    g, ag = oracle.gemm_nvfp4(gu.codes, gu.scales, gu.g, a_bits, rows=f)
+    u, au = oracle.gemm_nvfp4(gu.codes, gu.scales, gu.g, a_bits, rows=F + f)
+    s_ref = chain.bf16_round(chain.silu(g) * u)
+    s_gpu = chain.bf16_value(s_bits[:, f])
+    eg, eu = 1e-3 * ag, 1e-3 * au
+    bound = 1.1 * np.abs(u) * eg + (np.abs(chain.silu(g)) + 1.1 * eg) * eu + 2.0 ** -7 * np.maximum(
+        np.abs(s_ref), np.abs(s_gpu)) + 1e-37
+    worst_s = float((np.abs(s_gpu - s_ref) / bound).max())
+    m = np.unique(np.concatenate([rng.integers(0, D, check_rows), [0, D - 1]]))
+    y, ay = oracle.gemm_nvfp4(dn.codes, dn.scales, dn.g, s_bits, rows=m)
+    href = h0_host[:, m].astype(np.float64) + y
+    bound = 1e-3 * ay + 2.0 ** -23 * (np.abs(h0_host[:, m]) + np.abs(y)) + 1e-37
+    worst_h = float((np.abs(h1[:, m] - href) / bound).max())
+    ok = ok and worst_s <= 1.0 and worst_h <= 1.0
+    return {"name": "chained MLP verify pass: %d layers x (RMSNorm, gate+up %dx%d, SwiGLU, down %dx%d, residual)"
+                    % (layers, 2 * F, D, D, F),
+            "per_n": rows, "parity_ok": bool(ok), "layer0_max_err_over_bound": {"s": worst_s, "h": worst_h},
+            "probe_read_gbps": probe_gbps}
+
+
 # ---- main ------------------------------------------------------------------------
 
 def main():
@@ -485,6 +599,7 @@ def main():
     ap.add_argument("--check-rows", type=int, default=32, help="sampled rows per matrix checked against the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-product workloads 0, 1, 2, 4")
+    ap.add_argument("--no-chain", action="store_true", help="skip the chained MLP pass")
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
     args = ap.parse_args()
 
@@ -642,6 +757,10 @@ def main():
               "bound": "|y - y_oracle| <= 1e-3 * sum|w*x|"}
 
     device_n = device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n)
+    chained = None
+    if not args.no_chain:
+        chained = chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps)
+        ok = ok and chained["parity_ok"]
     draft = None
     singles = quant = None
     if not args.no_single:
@@ -683,6 +802,7 @@ def main():
         "parity": parity,
         "per_n_device_count": device_n,
         "draft_step": draft,
+        "chained_mlp": chained,
         "single_products": singles,
         "quantizers": quant,
     }

@@ -335,7 +335,8 @@ Split chain_down_split(int D, int F, int cus) {
 struct ChainLayout {
   Split gate_up, down;
   int grid_gate_up = 0, grid_down = 0, parts = 0;
-  size_t table_bytes = 0, ranges_gu_bytes = 0, ranges_down_bytes = 0, part_bytes = 0, ssp_bytes = 0, total = 0;
+  size_t table_bytes = 0, ranges_gu_bytes = 0, ranges_down_bytes = 0, ctl_bytes = 0, part_bytes = 0, ssp_bytes = 0,
+         total = 0;
 };
 
 wq_status check_chain_shape(int layers, int D, int F, int N) {
@@ -356,9 +357,10 @@ ChainLayout chain_layout(int layers, int D, int F, int N, int cus) {
   L.table_bytes = align_up((size_t)2 * layers * sizeof(DevMat), kAlign);
   L.ranges_gu_bytes = align_up((size_t)(L.grid_gate_up + 1) * sizeof(WgRange), kAlign);
   L.ranges_down_bytes = align_up((size_t)(L.grid_down + 1) * sizeof(WgRange), kAlign);
+  L.ctl_bytes = align_up(sizeof(ChainCtl), kAlign);
   L.part_bytes = align_up((size_t)L.down.nchunks * N * D * sizeof(float), kAlign);
   L.ssp_bytes = align_up((size_t)N * L.parts * sizeof(float), kAlign);
-  L.total = L.table_bytes + L.ranges_gu_bytes + L.ranges_down_bytes + L.part_bytes + L.ssp_bytes;
+  L.total = L.table_bytes + L.ranges_gu_bytes + L.ranges_down_bytes + L.ctl_bytes + L.part_bytes + L.ssp_bytes;
   return L;
 }
 
@@ -632,7 +634,8 @@ wq_status wq_mlp_chain_prepare(const wq_mlp_layer* layers, int count, int D, int
   char* ws = static_cast<char*>(workspace);
   const size_t off_rgu = L.table_bytes;
   const size_t off_rdn = off_rgu + L.ranges_gu_bytes;
-  const size_t off_part = off_rdn + L.ranges_down_bytes;
+  const size_t off_ctl = off_rdn + L.ranges_down_bytes;
+  const size_t off_part = off_ctl + L.ctl_bytes;
   const size_t off_ssp = off_part + L.part_bytes;
   float* part = reinterpret_cast<float*>(ws + off_part);
   float* ssp = reinterpret_cast<float*>(ws + off_ssp);
@@ -679,10 +682,13 @@ wq_status wq_mlp_chain_prepare(const wq_mlp_layer* layers, int count, int D, int
   plan->grid_gate_up = L.grid_gate_up;
   plan->grid_down = L.grid_down;
   plan->down_chunks = L.down.nchunks;
-  plan->reserved = 0;
+  // the single-launch chain: as many workgroups as stay resident (all CUs)
+  const int per_cu = chain_persistent_blocks_per_cu(N);
+  plan->grid_chain = per_cu > 0 ? cus * std::min(per_cu, 1) : 0;
   plan->ranges_gate_up_offset = off_rgu;
   plan->ranges_down_offset = off_rdn;
   plan->ssp_offset = off_ssp;
+  plan->ctl_offset = off_ctl;
   return WQ_SUCCESS;
 }
 
@@ -708,6 +714,20 @@ wq_status wq_mlp_chain_launch(const wq_mlp_plan* plan, void* stream) {
       e = launch_stream(N, kModeTiledWide, mats + 2 * l + 1, rdn, none, plan->grid_down, lds_bytes_for(N), s);
     if (e == hipSuccess) e = launch_chain_reduce(plan->h, mats + 2 * l + 1, plan->D, N, ssp, s);
   }
+  return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+wq_status wq_mlp_chain_launch_persistent(const wq_mlp_plan* plan, void* stream) {
+  if (!plan || !plan->workspace || !plan->h || plan->layers < 1 || plan->N < 1 || plan->N > 8 || plan->D < 1 ||
+      plan->grid_chain < 0 || plan->ssp_offset >= plan->workspace_bytes || plan->ctl_offset >= plan->workspace_bytes ||
+      ((plan->ctl_offset | plan->ssp_offset) & 15u))
+    return WQ_ERROR_INVALID_VALUE;
+  if (plan->grid_chain == 0) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  char* ws = static_cast<char*>(plan->workspace);
+  const hipError_t e = launch_chain_persistent(plan->N, reinterpret_cast<const DevMat*>(ws),
+                                               reinterpret_cast<ChainCtl*>(ws + plan->ctl_offset), plan->h,
+                                               reinterpret_cast<float*>(ws + plan->ssp_offset), plan->layers, plan->D,
+                                               plan->grid_chain, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
 }
 

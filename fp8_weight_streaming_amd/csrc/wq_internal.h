@@ -160,6 +160,16 @@ constexpr int waves_for_mode(int mode) {
 // kChainThreads outputs of one column; also each block's sum of squares.
 constexpr int kChainThreads = 256;
 
+// Grid barrier of the single-launch chain (in the workspace, zero before
+// the first launch): arrivals of the current barrier, barriers completed,
+// and a sticky flag set if a wait gave up (see kSpinLimit).
+struct ChainCtl {
+  uint32_t count;
+  uint32_t gen;
+  uint32_t error;
+  uint32_t pad;
+};
+
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevMat& one, int grid, int N,
@@ -172,6 +182,11 @@ hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const in
 // then ssp[n][p] = sum of h[n][m]^2 over block p's outputs.  down == null:
 // ssp only.
 hipError_t launch_chain_reduce(float* h, const DevMat* down, int D, int N, float* ssp, hipStream_t stream);
+// All layers of a chain in one cooperative launch of `grid` workgroups.
+hipError_t launch_chain_persistent(int N, const DevMat* mats, ChainCtl* ctl, float* h, float* ssp, int layers, int D,
+                                   int grid, hipStream_t stream);
+// Workgroups of the single-launch chain that fit on the device at once.
+int chain_persistent_blocks_per_cu(int N);
 hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t* drafts, int32_t* tokens,
                          int32_t* accepted, hipStream_t stream);
 

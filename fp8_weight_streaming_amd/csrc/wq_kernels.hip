@@ -175,22 +175,31 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 // ---- staging of an RMS-normalized X (chained MLP layers) -----------------
 // X[n][k] = BF16(h[n][k] * r[n] * gamma[k]), r[n] = 1 / sqrt(ss[n] / K + eps),
 // with ss[n] the sum of the nparts partial sums of squares of column n
-// (added in order) -- the RMSNorm of a pre-norm transformer layer, computed
+// -- the RMSNorm of a pre-norm transformer layer, computed
 // once per workgroup from the FP32 residual stream instead of by a kernel of
 // its own.  Every workgroup computes the same bits; the pieces of 16 bytes
-// numbered 256j .. 256j + 255 are also written to aout by workgroup
-// j mod gridDim.x, so that the normalized input is visible to the caller.
+// numbered 256j .. 256j + 255 are also written to aout by the workgroup
+// whose units [u0, u1) hold unit j mod units (the units of all workgroups
+// partition the matrix's), so that the normalized input is visible to the
+// caller.
 // r[n] goes to the 512 bytes past the zero block.  Every thread calls this.
 constexpr int kNormLoads = 4;
 template <int N>
-__device__ void stage_norm(char* lds, const DevMat& mt, int kc_pad) {
+__device__ void stage_norm(char* lds, const DevMat& mt, int kc_pad, int64_t u0, int64_t u1, int64_t units) {
   float* rl = reinterpret_cast<float*>(lds + kZeroOffset<N>() + kZeroBytes<N>());
   const int K = mt.K;
-  if (threadIdx.x < N) {
-    const float* sp = mt.ssp + (size_t)threadIdx.x * mt.nparts;
-    float ss = 0.0f;
-    for (int p = 0; p < mt.nparts; ++p) ss += sp[p];
-    rl[threadIdx.x] = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(ss, (float)K) + mt.eps));
+  // wave n sums column n's partials: lane l takes p = l, l + 64, ..., then
+  // a butterfly over the lanes (a fixed order, so every workgroup agrees)
+  {
+    const int wv = (int)(threadIdx.x >> 6), ln = (int)(threadIdx.x & 63);
+    if (wv < N) {
+      const float* sp = mt.ssp + (size_t)wv * mt.nparts;
+      float ss = 0.0f;
+      for (int p = ln; p < mt.nparts; p += 64) ss += sp[p];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+      if (ln == 0) rl[wv] = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(ss, (float)K) + mt.eps));
+    }
   }
   __syncthreads();
   const int valid = K / 8;
@@ -227,8 +236,8 @@ __device__ void stage_norm(char* lds, const DevMat& mt, int kc_pad) {
           const float lo = (hv[2 * i] * r) * glo, hi = (hv[2 * i + 1] * r) * ghi;
           o[i] = bf16_rne(lo) | (bf16_rne(hi) << 16);
         }
-        if (((p >> 8) % (int)gridDim.x) == (int)blockIdx.x)
-          *reinterpret_cast<u32x4*>(mt.aout + (size_t)n * K + 8 * kc) = o;
+        const int64_t owner = (int64_t)(p >> 8) % units;
+        if (owner >= u0 && owner < u1) *reinterpret_cast<u32x4*>(mt.aout + (size_t)n * K + 8 * kc) = o;
       }
       *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = o;
     }
@@ -703,13 +712,65 @@ __device__ void fp8_unit(const DevMat& mt, int chunk, int tile, const char* lds)
   finish_tile<N>(mt, chunk, tile, sum, rsc);
 }
 
+// ---- grid barrier of the single-launch chain --------------------------------
+// A split barrier: a workgroup arrives once its stores of a phase are
+// issued and waits, later, before it reads what the other workgroups stored
+// (so that it can issue its next weight loads in between).  count holds the
+// arrivals at the open barrier; the last arrival resets it and advances gen,
+// which the waiting workgroups watch.  Every wait is bounded: after
+// kSpinLimit polls it sets ctl->error and goes on, so that the grid always
+// drains even if a workgroup never arrives (the results are then not
+// defined).  Only a launch that keeps every workgroup resident (a
+// cooperative launch) may use it.
+struct GridSync {
+  ChainCtl* ctl;
+  uint32_t* s_gen;  // LDS: gen as read at this workgroup's last arrival
+};
+constexpr uint32_t kSpinLimit = 1u << 19;
+
+__device__ __forceinline__ void grid_arrive(const GridSync& gs) {
+  __threadfence();  // this thread's stores are visible device-wide
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ChainCtl* c = gs.ctl;
+    *gs.s_gen = __hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(&c->count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
+      __hip_atomic_store(&c->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&c->gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__device__ __forceinline__ void grid_wait(const GridSync& gs) {
+  if (threadIdx.x == 0) {
+    ChainCtl* c = gs.ctl;
+    const uint32_t g = *gs.s_gen;
+    // (relaxed polls, so that a poll does not invalidate the caches; the
+    // acquire fence below orders what follows after the change was seen)
+    for (uint32_t it = 0; __hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g; ++it) {
+      if (it == kSpinLimit) {
+        __hip_atomic_fetch_or(&c->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 // ---- the persistent kernel -------------------------------------------------
 // Workgroup w processes units [range[w].begin, range[w+1].begin) of the
 // global unit list (matrix-major, then chunk, then tile).  For a single
 // matrix (mats == nullptr) the split is computed here, equal by units.
-template <int N, int MODE>
+// SYNC (the single-launch chain, one matrix, no ranges table: equal
+// shares): the first staging of the call first waits at the grid barrier
+// (the matrix's X is made by the previous phase), after the run's first
+// weight loads are issued; a workgroup with no units waits at the end.
+template <int N, int MODE, bool SYNC = false>
 __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, const WgRange* __restrict__ ranges,
-                                            const DevMat& one, char* lds) {
+                                            const DevMat& one, char* lds, const GridSync* gs = nullptr) {
   // wave-uniform values are pinned to scalar registers so that buffer
   // resources built from them stay uniform
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -717,8 +778,8 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
 
   int64_t u, u_end;
   int mi;
-  if (mats == nullptr) {
-    const int64_t total = (int64_t)one.nchunks * one.ntiles;
+  if (mats == nullptr || ranges == nullptr) {
+    const int64_t total = mats ? (int64_t)mats[0].nchunks * mats[0].ntiles : (int64_t)one.nchunks * one.ntiles;
     u = total * blockIdx.x / gridDim.x;
     u_end = total * (blockIdx.x + 1) / gridDim.x;
     mi = 0;
@@ -742,6 +803,19 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
                             ? reinterpret_cast<DynSched*>(const_cast<WgRange*>(ranges) + gridDim.x + 1)
                             : nullptr;
   __shared__ uint32_t s_claim;
+  bool waited = false;
+  // the barrier at the start of a staging (protects the LDS still read by
+  // the previous run; with SYNC the first one is the grid barrier)
+  auto sync_first = [&]() {
+    if constexpr (SYNC) {
+      if (!waited) {
+        waited = true;
+        grid_wait(*gs);
+        return;
+      }
+    }
+    __syncthreads();
+  };
 
   for (;;) {
   while (u < u_end) {
@@ -763,7 +837,7 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     // every wave calls this once per run (the barriers protect the LDS
     // still read by the previous run, then publish the new X)
     auto stage = [&]() {
-      __syncthreads();
+      sync_first();
       stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
       __syncthreads();
     };
@@ -783,8 +857,8 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
         tiled_run<N, kPrefetchTiled, false, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, stage);
     } else if constexpr (MODE == kModeTiledGlu) {
       auto stage_norm_x = [&]() {
-        __syncthreads();
-        stage_norm<N>(lds, mt, kc_pad);
+        sync_first();
+        stage_norm<N>(lds, mt, kc_pad, u - mt.unit0, run_end - mt.unit0, (int64_t)mt.nchunks * mt.ntiles);
         __syncthreads();
       };
       tiled_run<N, kPrefetchWide, false, kEpiGlu>(mt, chunk, share0, share1, lds, bestk, stage_norm_x);
@@ -834,6 +908,9 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
   u = dyn->begin + (int64_t)idx * dyn->chunk;
   u_end = min(u + (int64_t)dyn->chunk, dyn->end);
   mi = reinterpret_cast<const int32_t*>(dyn + 1)[idx];
+  }
+  if constexpr (SYNC) {
+    if (!waited) grid_wait(*gs);
   }
   // The last workgroup to finish sets the counters back for the next launch.
   // Every workgroup's final claim has returned before its `done` increment
@@ -921,16 +998,18 @@ __global__ __launch_bounds__(kThreadsTiled) void stream_kernel_dyn(const DevMat*
 // for a down product split in K (one chunk: its y, already scaled, is
 // added), and writes the sum of their squares (after the update) to
 // ssp[n][p], the partials from which the next layer's RMSNorm takes its
-// scale (summed in p order).  With no descriptor it only writes ssp.  The
+// scale.  With no descriptor it only writes ssp.  The
 // sum over a block is a fixed tree (butterfly within a wave, then the waves
 // in order), so every run gives the same bits.
-__global__ __launch_bounds__(kChainThreads) void chain_reduce_kernel(float* __restrict__ h,
-                                                                     const DevMat* __restrict__ down, int D, int N,
-                                                                     float* __restrict__ ssp) {
-  const int n = blockIdx.y, p = blockIdx.x;
-  const int m = p * kChainThreads + (int)threadIdx.x;
+// The work of block (p, n) as above, by threads 0 .. kChainThreads - 1 of the
+// calling workgroup (every thread calls it: it holds two barriers).
+__device__ __forceinline__ void chain_reduce_block(float* __restrict__ h, const DevMat* __restrict__ down, int D,
+                                                   int N, int n, int p, int P, float* __restrict__ ssp,
+                                                   float* wsum) {
+  const int t = (int)threadIdx.x;
+  const int m = p * kChainThreads + t;
   float v = 0.0f;
-  if (m < D) {
+  if (t < kChainThreads && m < D) {
     const size_t o = (size_t)n * D + m;
     v = h[o];
     if (down) {
@@ -949,13 +1028,51 @@ __global__ __launch_bounds__(kChainThreads) void chain_reduce_kernel(float* __re
   float sq = v * v;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
-  __shared__ float wsum[kChainThreads / 64];
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = sq;
+  if (t < kChainThreads && (t & 63) == 0) wsum[t >> 6] = sq;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float t = 0.0f;
-    for (int w = 0; w < kChainThreads / 64; ++w) t += wsum[w];
-    ssp[(size_t)n * gridDim.x + p] = t;
+  if (t == 0) {
+    float s = 0.0f;
+    for (int w = 0; w < kChainThreads / 64; ++w) s += wsum[w];
+    ssp[(size_t)n * P + p] = s;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kChainThreads) void chain_reduce_kernel(float* __restrict__ h,
+                                                                     const DevMat* __restrict__ down, int D, int N,
+                                                                     float* __restrict__ ssp) {
+  __shared__ float wsum[kChainThreads / 64];
+  chain_reduce_block(h, down, D, N, blockIdx.y, blockIdx.x, gridDim.x, ssp, wsum);
+}
+
+// ---- a whole chain in one launch ------------------------------------------------
+// The phases of the multi-launch chain, in the same order and with the same
+// arithmetic (so the same bits), with a grid barrier between phases instead
+// of a kernel boundary: the sums of squares of h; then per layer the
+// gate/up phase (its first weight loads issued before the barrier that
+// publishes h), the down phase (likewise for s), and the residual update.
+// Shares of the streaming phases are equal splits of each matrix's units.
+template <int N>
+__global__ __launch_bounds__(kThreads) void chain_kernel(const DevMat* __restrict__ mats, ChainCtl* ctl,
+                                                         float* __restrict__ h, float* __restrict__ ssp, int layers,
+                                                         int D) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ uint32_t s_gen;
+  __shared__ float wsum[kChainThreads / 64];
+  const GridSync gs{ctl, &s_gen};
+  const int P = (D + kChainThreads - 1) / kChainThreads;
+  const DevMat none{};
+  for (int b = blockIdx.x; b < N * P; b += gridDim.x) chain_reduce_block(h, nullptr, D, N, b / P, b % P, P, ssp, wsum);
+  grid_arrive(gs);
+  for (int l = 0; l < layers; ++l) {
+    stream_body<N, kModeTiledGlu, true>(mats + 2 * l, nullptr, none, lds, &gs);
+    grid_arrive(gs);
+    stream_body<N, kModeTiledWide, true>(mats + 2 * l + 1, nullptr, none, lds, &gs);
+    grid_arrive(gs);
+    grid_wait(gs);
+    for (int b = blockIdx.x; b < N * P; b += gridDim.x)
+      chain_reduce_block(h, mats + 2 * l + 1, D, N, b / P, b % P, P, ssp, wsum);
+    if (l + 1 < layers) grid_arrive(gs);
   }
 }
 
@@ -1026,6 +1143,61 @@ hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const in
   hipLaunchKernelGGL(stream_kernel_dyn, dim3(grid), dim3(kThreadsTiled), lds_bytes_for(8), stream, mats, ranges,
                      n_dev);
   return hipGetLastError();
+}
+
+template <int N>
+static std::atomic<uint64_t>& chain_lds_set() {
+  static std::atomic<uint64_t> done{0};
+  return done;
+}
+
+template <int N>
+static hipError_t launch_chain_n(const DevMat* mats, ChainCtl* ctl, float* h, float* ssp, int layers, int D, int grid,
+                                 hipStream_t stream) {
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&chain_kernel<N>), chain_lds_set<N>());
+  if (e != hipSuccess) return e;
+  void* args[] = {&mats, &ctl, &h, &ssp, &layers, &D};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&chain_kernel<N>), dim3(grid), dim3(kThreads), args,
+                                    lds_bytes_for(N) + kArgLdsBytes, stream);
+}
+
+template <int N>
+static int chain_blocks_n() {
+  if (allow_lds(reinterpret_cast<const void*>(&chain_kernel<N>), chain_lds_set<N>()) != hipSuccess) return 0;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&chain_kernel<N>), kThreads,
+                                                   lds_bytes_for(N) + kArgLdsBytes) != hipSuccess)
+    return 0;
+  return nb;
+}
+
+hipError_t launch_chain_persistent(int N, const DevMat* mats, ChainCtl* ctl, float* h, float* ssp, int layers, int D,
+                                   int grid, hipStream_t stream) {
+  switch (N) {
+    case 1: return launch_chain_n<1>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 2: return launch_chain_n<2>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 3: return launch_chain_n<3>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 4: return launch_chain_n<4>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 5: return launch_chain_n<5>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 6: return launch_chain_n<6>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 7: return launch_chain_n<7>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 8: return launch_chain_n<8>(mats, ctl, h, ssp, layers, D, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int chain_persistent_blocks_per_cu(int N) {
+  switch (N) {
+    case 1: return chain_blocks_n<1>();
+    case 2: return chain_blocks_n<2>();
+    case 3: return chain_blocks_n<3>();
+    case 4: return chain_blocks_n<4>();
+    case 5: return chain_blocks_n<5>();
+    case 6: return chain_blocks_n<6>();
+    case 7: return chain_blocks_n<7>();
+    case 8: return chain_blocks_n<8>();
+    default: return 0;
+  }
 }
 
 // ---- greedy draft acceptance -------------------------------------------------

@@ -68,8 +68,9 @@ class WqMlpPlan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("h", ctypes.c_void_p),
                 ("layers", ctypes.c_int32), ("D", ctypes.c_int32), ("F", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("grid_gate_up", ctypes.c_int32), ("grid_down", ctypes.c_int32), ("down_chunks", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("ranges_gate_up_offset", ctypes.c_size_t),
-                ("ranges_down_offset", ctypes.c_size_t), ("ssp_offset", ctypes.c_size_t)]
+                ("grid_chain", ctypes.c_int32), ("ranges_gate_up_offset", ctypes.c_size_t),
+                ("ranges_down_offset", ctypes.c_size_t), ("ssp_offset", ctypes.c_size_t),
+                ("ctl_offset", ctypes.c_size_t)]
 
 
 _P = ctypes.c_void_p
@@ -139,12 +140,14 @@ _lib.wq_mlp_chain_prepare.argtypes = [ctypes.POINTER(WqMlpLayer), _I, _I, _I, _I
                                       _S, _P, ctypes.POINTER(WqMlpPlan)]
 _lib.wq_mlp_chain_launch.restype = _I
 _lib.wq_mlp_chain_launch.argtypes = [ctypes.POINTER(WqMlpPlan), _P]
+_lib.wq_mlp_chain_launch_persistent.restype = _I
+_lib.wq_mlp_chain_launch_persistent.argtypes = [ctypes.POINTER(WqMlpPlan), _P]
 
 EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
             "wq_head_accept_workspace_bytes", "wq_head_accept", "wq_quantize_fp8row", "wq_quantize_nvfp4",
             "wq_verify_launch_n", "wq_nvfp4_tile_glu", "wq_mlp_chain_workspace_bytes", "wq_mlp_chain_split",
-            "wq_mlp_chain_prepare", "wq_mlp_chain_launch",
+            "wq_mlp_chain_prepare", "wq_mlp_chain_launch", "wq_mlp_chain_launch_persistent",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
 
@@ -450,3 +453,8 @@ def wq_mlp_chain_prepare(layers: Sequence[MlpLayer], D: int, F: int, N: int, eps
 def wq_mlp_chain_launch(plan: WqMlpPlan, stream=None):
     """Run the prepared layers (launches only); updates h in place."""
     _check(_lib.wq_mlp_chain_launch(ctypes.byref(plan), _stream(stream)), "wq_mlp_chain_launch")
+
+
+def wq_mlp_chain_launch_persistent(plan: WqMlpPlan, stream=None):
+    """Run the prepared layers in one cooperative launch; updates h in place."""
+    _check(_lib.wq_mlp_chain_launch_persistent(ctypes.byref(plan), _stream(stream)), "wq_mlp_chain_launch_persistent")

@@ -328,7 +328,19 @@ wq_status wq_quantize_nvfp4(const uint16_t* w, int M, int K, float global_scale,
  *   alive).  Each run updates h in place.  Results are deterministic, and
  *   running the layers in one call or one layer per call gives the same
  *   bits.  An all-zero column with eps = 0 gives NaN (0 * inf), as the
- *   formula does. */
+ *   formula does.
+ * wq_mlp_chain_launch_persistent: the same layers, phases and bits in ONE
+ *   cooperative launch (every workgroup resident), whose phases are
+ *   separated by grid barriers in the workspace instead of kernel
+ *   boundaries, so that each phase's first weight loads are in flight
+ *   while the previous phase finishes (the card's "Decode" row: a round as
+ *   one device-side program).  Returns WQ_ERROR_UNSUPPORTED_SHAPE when the
+ *   device cannot keep the grid resident (plan->grid_chain == 0).  A wait
+ *   that gives up (a workgroup that never arrives, which a correct launch
+ *   does not produce) sets the uint32 at workspace + plan->ctl_offset + 8
+ *   to nonzero instead of hanging; the outputs are then undefined and the
+ *   plan must be prepared again.  Launches of one plan must not overlap.
+ *   Not for stream capture. */
 typedef struct wq_mlp_layer {
   const void* gate_up;    /* from wq_nvfp4_tile_glu */
   const void* down;       /* from wq_nvfp4_tile, D x F */
@@ -350,10 +362,11 @@ typedef struct wq_mlp_plan {
   int32_t grid_gate_up;
   int32_t grid_down;
   int32_t down_chunks;
-  int32_t reserved;
+  int32_t grid_chain;
   size_t ranges_gate_up_offset;
   size_t ranges_down_offset;
   size_t ssp_offset;
+  size_t ctl_offset;
 } wq_mlp_plan;
 
 wq_status wq_nvfp4_tile_glu(const uint8_t* gate_codes, const uint8_t* gate_scales, const uint8_t* up_codes,
@@ -365,6 +378,7 @@ wq_status wq_mlp_chain_prepare(const wq_mlp_layer* layers, int count, int D, int
                                float* h, uint16_t* a, uint16_t* s, void* workspace, size_t workspace_bytes,
                                void* stream, wq_mlp_plan* plan);
 wq_status wq_mlp_chain_launch(const wq_mlp_plan* plan, void* stream);
+wq_status wq_mlp_chain_launch_persistent(const wq_mlp_plan* plan, void* stream);
 
 /* Measurement kernels (not part of the product; they price it).  The crit
  * README's Eval turns the GPU's measured bandwidth into a floor for each

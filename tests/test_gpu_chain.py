@@ -57,8 +57,9 @@ class Layer:
         return t(self.inp.gate), t(self.inp.up), t(self.inp.down)
 
 
-def run_chain(wq, layers, h0, stream=None):
-    """Runs the layers on columns h0 [N][D]; returns (h, a, s) as numpy."""
+def run_chain(wq, layers, h0, stream=None, persistent=False):
+    """Runs the layers on columns h0 [N][D]; returns (h, a, s) as numpy
+    (one launch per kernel, or the single cooperative launch)."""
     N, D = h0.shape
     F = layers[0].F
     h = dev_f32(h0)
@@ -66,8 +67,15 @@ def run_chain(wq, layers, h0, stream=None):
     s = torch.full((N, F), -1, dtype=torch.int16, device=DEV)
     ws = torch.empty(wq.wq_mlp_chain_workspace_bytes(len(layers), D, F, N), dtype=torch.uint8, device=DEV)
     plan = wq.wq_mlp_chain_prepare([y.desc for y in layers], D, F, N, EPS, h, a, s, ws)
-    wq.wq_mlp_chain_launch(plan)
+    if persistent:
+        assert plan.grid_chain > 0
+        wq.wq_mlp_chain_launch_persistent(plan)
+    else:
+        wq.wq_mlp_chain_launch(plan)
     torch.cuda.synchronize()
+    if persistent:
+        ctl = ws[plan.ctl_offset:plan.ctl_offset + 16].cpu().numpy().view(np.uint32)
+        assert ctl[0] == 0 and ctl[2] == 0, "grid barrier state %s" % ctl.tolist()
     return (h.cpu().numpy(), a.cpu().numpy().view(np.uint16), s.cpu().numpy().view(np.uint16))
 
 
@@ -206,3 +214,33 @@ def test_zero_down_weights_pass_the_residual_through(wq):
     a_ref = chain.normalize(h0, layer.inp.gamma, EPS)
     assert np.all(np.abs(chain.bf16_value(a) - a_ref) <= 2.0 ** -7 * np.abs(a_ref))
     assert np.any(s != 0)
+
+
+# ---- the single-launch chain ------------------------------------------------------
+
+@pytest.mark.parametrize("D,F,N,L", [(32, 32, 1, 1), (64, 96, 3, 2), (320, 544, 8, 3), (1024, 4352, 5, 2)])
+def test_single_launch_equals_launch_per_kernel(wq, D, F, N, L):
+    # small shapes leave most workgroups without units in a phase: they
+    # must still take part in every grid barrier
+    print("single-launch chain D=%d F=%d N=%d L=%d" % (D, F, N, L), flush=True)
+    layers = [Layer(wq, D, F, seed=200 + 7 * i + D) for i in range(L)]
+    h0 = inputs.residual_inputs(N, D, seed=201)
+    ref = run_chain(wq, layers, h0)
+    got = run_chain(wq, layers, h0, persistent=True)
+    for x, y in zip(ref, got):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_single_launch_full_size_and_repeat(wq):
+    D, F, N = 5120, 17408, 8
+    print("single-launch chain full size", flush=True)
+    layers = [Layer(wq, D, F, seed=300 + i) for i in range(3)]
+    h0 = inputs.residual_inputs(N, D, seed=301)
+    h1, a1, s1 = run_chain(wq, layers[:1], h0, persistent=True)
+    check_layer(layers[0], h0, h1, a1, s1, "single-launch full layer 0")
+    ref = run_chain(wq, layers, h0)
+    for rep in range(2):
+        got = run_chain(wq, layers, h0, persistent=True)
+        for x, y in zip(ref, got):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), rep
+
