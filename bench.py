@@ -540,12 +540,24 @@ def chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=48,
             e1.record(stream)
         torch.cuda.synchronize()
         graph_us = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
+        single_us = None
+        if plan.grid_chain > 0:
+            wq.wq_mlp_chain_launch_persistent(plan, stream)
+            for e0, e1 in ev:
+                h.copy_(h0)
+                e0.record(stream)
+                wq.wq_mlp_chain_launch_persistent(plan, stream)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            single_us = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
         nb = chain_bytes(D, F, N, layers)
         kc, nc = wq.wq_mlp_chain_split(D, F)
         rows[str(N)] = {"eager_us": eager_us, "graph_us": graph_us, "us_per_layer_graph": graph_us / layers,
                         "algorithmic_bytes": nb, "gbps_graph": nb / graph_us / 1e3,
                         "pct_of_8TBps_graph": 100 * nb / graph_us / 1e3 / PEAK_GBPS,
                         "pct_of_8TBps_eager": 100 * nb / eager_us / 1e3 / PEAK_GBPS,
+                        "single_launch_us": single_us,
+                        "pct_of_8TBps_single_launch": (100 * nb / single_us / 1e3 / PEAK_GBPS) if single_us else None,
                         "launches": 3 * layers + 1, "down_k_chunks": nc}
         del graph, ws, plan
 

@@ -140,28 +140,54 @@ __device__ __forceinline__ bf16x8 lds_read16(const char* lds, uint32_t off) {
 // LDS layout: piece (kc, n) = X[n][k0 + 8kc .. k0 + 8kc + 7] (16 bytes) at
 // byte (kc * N + n) * 16, for kc < kc_pad (pieces past the chunk are zero).
 constexpr int kStageLoads = 8;
+// One batch: the pieces p0 + j * blockDim.x, j < kStageLoads, into registers
+// (eight 16-byte loads in flight per thread before any LDS store: staging
+// is a few rounds of L2/HBM latency, and at the start of every run) ...
 template <int N>
-__device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0, int klen, int kc_pad) {
+__device__ __forceinline__ void stage_x_load(u32x4 (&v)[kStageLoads], const uint16_t* __restrict__ x, int K, int k0,
+                                             int klen, int kc_pad, int p0) {
   const int valid = klen / 8;
   const int total = kc_pad * N;
-  // eight 16-byte loads in flight per thread before any LDS store: staging
-  // is a few rounds of L2/HBM latency, and at the start of every run
-  for (int p0 = threadIdx.x; p0 < total; p0 += kStageLoads * (int)blockDim.x) {
+#pragma unroll
+  for (int j = 0; j < kStageLoads; ++j) {
+    const int p = p0 + j * (int)blockDim.x;
+    const int n = p / kc_pad, kc = p - n * kc_pad;
+    v[j] = u32x4{0u, 0u, 0u, 0u};
+    if (p < total && kc < valid) v[j] = *reinterpret_cast<const u32x4*>(x + (size_t)n * K + k0 + 8 * kc);
+  }
+}
+// ... and from registers into LDS.
+template <int N>
+__device__ __forceinline__ void stage_x_store(const u32x4 (&v)[kStageLoads], char* lds, int kc_pad, int p0) {
+  const int total = kc_pad * N;
+#pragma unroll
+  for (int j = 0; j < kStageLoads; ++j) {
+    const int p = p0 + j * (int)blockDim.x;
+    const int n = p / kc_pad, kc = p - n * kc_pad;
+    if (p < total) *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = v[j];
+  }
+}
+// The batches after the first, whose registers v0 were loaded earlier (the
+// tiled runs load them before their first weight loads, so that X, needed
+// first, is not queued behind the weights).
+template <int N>
+__device__ void stage_x_rest(const u32x4 (&v0)[kStageLoads], char* lds, const uint16_t* __restrict__ x, int K, int k0,
+                             int klen, int kc_pad) {
+  stage_x_store<N>(v0, lds, kc_pad, (int)threadIdx.x);
+  for (int p0 = (int)threadIdx.x + kStageLoads * (int)blockDim.x; p0 < kc_pad * N;
+       p0 += kStageLoads * (int)blockDim.x) {
     u32x4 v[kStageLoads];
-#pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) {
-      const int p = p0 + j * (int)blockDim.x;
-      const int n = p / kc_pad, kc = p - n * kc_pad;
-      v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (p < total && kc < valid)
-        v[j] = *reinterpret_cast<const u32x4*>(x + (size_t)n * K + k0 + 8 * kc);
-    }
-#pragma unroll
-    for (int j = 0; j < kStageLoads; ++j) {
-      const int p = p0 + j * (int)blockDim.x;
-      const int n = p / kc_pad, kc = p - n * kc_pad;
-      if (p < total) *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = v[j];
-    }
+    stage_x_load<N>(v, x, K, k0, klen, kc_pad, p0);
+    stage_x_store<N>(v, lds, kc_pad, p0);
+  }
+}
+// All batches (the plain-layout kernels).
+template <int N>
+__device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0, int klen, int kc_pad) {
+  for (int p0 = threadIdx.x; p0 < kc_pad * N; p0 += kStageLoads * (int)blockDim.x) {
+    u32x4 v[kStageLoads];
+    stage_x_load<N>(v, x, K, k0, klen, kc_pad, p0);
+    stage_x_store<N>(v, lds, kc_pad, p0);
   }
 }
 
@@ -183,64 +209,90 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 // partition the matrix's), so that the normalized input is visible to the
 // caller.
 // r[n] goes to the 512 bytes past the zero block.  Every thread calls this.
-constexpr int kNormLoads = 4;
+constexpr int kNormLoads = 2;
+// Registers of one batch (the first one is loaded before the run's first
+// weight loads): each lane's partial sum of squares (nparts <= 64: one per
+// lane) and the h / gamma pieces p0 + j * blockDim.x, j < kNormLoads.
+struct NormBatch {
+  f32x4 h0[kNormLoads], h1[kNormLoads];
+  u32x4 gm[kNormLoads];
+  float ss;
+};
 template <int N>
-__device__ void stage_norm(char* lds, const DevMat& mt, int kc_pad, int64_t u0, int64_t u1, int64_t units) {
-  float* rl = reinterpret_cast<float*>(lds + kZeroOffset<N>() + kZeroBytes<N>());
+__device__ __forceinline__ void norm_load(NormBatch& b, const DevMat& mt, int kc_pad, int p0) {
   const int K = mt.K;
-  // wave n sums column n's partials: lane l takes p = l, l + 64, ..., then
-  // a butterfly over the lanes (a fixed order, so every workgroup agrees)
+  const int valid = K / 8;
+  const int total = kc_pad * N;
+#pragma unroll
+  for (int j = 0; j < kNormLoads; ++j) {
+    const int p = p0 + j * (int)blockDim.x;
+    const int n = p / kc_pad, kc = p - n * kc_pad;
+    b.h0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    b.h1[j] = b.h0[j];
+    b.gm[j] = u32x4{0u, 0u, 0u, 0u};
+    if (p < total && kc < valid) {
+      const float* hp = mt.h + (size_t)n * K + 8 * kc;
+      b.h0[j] = *reinterpret_cast<const f32x4*>(hp);
+      b.h1[j] = *reinterpret_cast<const f32x4*>(hp + 4);
+      b.gm[j] = *reinterpret_cast<const u32x4*>(mt.gamma + 8 * kc);
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void norm_first(NormBatch& b, const DevMat& mt, int kc_pad) {
+  const int wv = (int)(threadIdx.x >> 6), ln = (int)(threadIdx.x & 63);
+  b.ss = (wv < N && ln < mt.nparts) ? mt.ssp[(size_t)wv * mt.nparts + ln] : 0.0f;
+  norm_load<N>(b, mt, kc_pad, (int)threadIdx.x);
+}
+template <int N>
+__device__ __forceinline__ void norm_store(const NormBatch& b, char* lds, const DevMat& mt, int kc_pad, int p0,
+                                           const float* rl, int64_t u0, int64_t u1, int64_t units) {
+  const int K = mt.K;
+  const int valid = K / 8;
+  const int total = kc_pad * N;
+#pragma unroll
+  for (int j = 0; j < kNormLoads; ++j) {
+    const int p = p0 + j * (int)blockDim.x;
+    if (p >= total) continue;
+    const int n = p / kc_pad, kc = p - n * kc_pad;
+    const float r = rl[n];
+    const float hv[8] = {b.h0[j].x, b.h0[j].y, b.h0[j].z, b.h0[j].w, b.h1[j].x, b.h1[j].y, b.h1[j].z, b.h1[j].w};
+    u32x4 o = {0u, 0u, 0u, 0u};
+    if (kc < valid) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float glo = __uint_as_float(b.gm[j][i] << 16), ghi = __uint_as_float(b.gm[j][i] & 0xFFFF0000u);
+        const float lo = (hv[2 * i] * r) * glo, hi = (hv[2 * i + 1] * r) * ghi;
+        o[i] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+      }
+      const int64_t owner = (int64_t)(p >> 8) % units;
+      if (owner >= u0 && owner < u1) *reinterpret_cast<u32x4*>(mt.aout + (size_t)n * K + 8 * kc) = o;
+    }
+    *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = o;
+  }
+}
+// Everything after norm_first (every thread calls it; it holds a barrier).
+template <int N>
+__device__ void stage_norm(NormBatch& b, char* lds, const DevMat& mt, int kc_pad, int64_t u0, int64_t u1,
+                           int64_t units) {
+  float* rl = reinterpret_cast<float*>(lds + kZeroOffset<N>() + kZeroBytes<N>());
+  // wave n sums column n's partials (lane l holds p = l; nparts <= 64) by a
+  // butterfly over the lanes (a fixed order, so every workgroup agrees)
   {
     const int wv = (int)(threadIdx.x >> 6), ln = (int)(threadIdx.x & 63);
     if (wv < N) {
-      const float* sp = mt.ssp + (size_t)wv * mt.nparts;
-      float ss = 0.0f;
-      for (int p = ln; p < mt.nparts; p += 64) ss += sp[p];
+      float ss = b.ss;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-      if (ln == 0) rl[wv] = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(ss, (float)K) + mt.eps));
+      if (ln == 0) rl[wv] = __fdiv_rn(1.0f, __fsqrt_rn(__fdiv_rn(ss, (float)mt.K) + mt.eps));
     }
   }
   __syncthreads();
-  const int valid = K / 8;
-  const int total = kc_pad * N;
-  for (int p0 = threadIdx.x; p0 < total; p0 += kNormLoads * (int)blockDim.x) {
-    f32x4 h0[kNormLoads], h1[kNormLoads];
-    u32x4 gm[kNormLoads];
-#pragma unroll
-    for (int j = 0; j < kNormLoads; ++j) {
-      const int p = p0 + j * (int)blockDim.x;
-      const int n = p / kc_pad, kc = p - n * kc_pad;
-      h0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      h1[j] = h0[j];
-      gm[j] = u32x4{0u, 0u, 0u, 0u};
-      if (p < total && kc < valid) {
-        const float* hp = mt.h + (size_t)n * K + 8 * kc;
-        h0[j] = *reinterpret_cast<const f32x4*>(hp);
-        h1[j] = *reinterpret_cast<const f32x4*>(hp + 4);
-        gm[j] = *reinterpret_cast<const u32x4*>(mt.gamma + 8 * kc);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kNormLoads; ++j) {
-      const int p = p0 + j * (int)blockDim.x;
-      if (p >= total) continue;
-      const int n = p / kc_pad, kc = p - n * kc_pad;
-      const float r = rl[n];
-      const float hv[8] = {h0[j].x, h0[j].y, h0[j].z, h0[j].w, h1[j].x, h1[j].y, h1[j].z, h1[j].w};
-      u32x4 o = {0u, 0u, 0u, 0u};
-      if (kc < valid) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float glo = __uint_as_float(gm[j][i] << 16), ghi = __uint_as_float(gm[j][i] & 0xFFFF0000u);
-          const float lo = (hv[2 * i] * r) * glo, hi = (hv[2 * i + 1] * r) * ghi;
-          o[i] = bf16_rne(lo) | (bf16_rne(hi) << 16);
-        }
-        const int64_t owner = (int64_t)(p >> 8) % units;
-        if (owner >= u0 && owner < u1) *reinterpret_cast<u32x4*>(mt.aout + (size_t)n * K + 8 * kc) = o;
-      }
-      *reinterpret_cast<u32x4*>(lds + (size_t)(kc * N + n) * 16) = o;
-    }
+  norm_store<N>(b, lds, mt, kc_pad, (int)threadIdx.x, rl, u0, u1, units);
+  for (int p0 = (int)threadIdx.x + kNormLoads * (int)blockDim.x; p0 < kc_pad * N;
+       p0 += kNormLoads * (int)blockDim.x) {
+    norm_load<N>(b, mt, kc_pad, p0);
+    norm_store<N>(b, lds, mt, kc_pad, p0, rl, u0, u1, units);
   }
 }
 
@@ -423,13 +475,16 @@ __device__ __forceinline__ uint64_t greedy_key(float v, int m) {
 //
 // stage() stages the run's X into LDS between two workgroup barriers.  The
 // run calls it once on every path, after issuing its first PF steps of
-// weight loads, so that their round trip overlaps the staging.
+// weight loads, so that their round trip overlaps the staging; pre(), called
+// first, issues the staging's first loads, so that X does not wait for the
+// weights (a wave's loads complete in order).
 constexpr int kEpiStore = 0;
 constexpr int kEpiArgmax = 1;
 constexpr int kEpiGlu = 2;
-template <int N, int PF, bool FP8, int EPI, typename Stage>
+template <int N, int PF, bool FP8, int EPI, typename Pre, typename Stage>
 __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds,
-                          uint64_t* bestk, Stage&& stage) {
+                          uint64_t* bestk, Pre&& pre, Stage&& stage) {
+  pre();
   if (first >= end) {
     stage();
     return;
@@ -728,11 +783,16 @@ struct GridSync {
 };
 constexpr uint32_t kSpinLimit = 1u << 19;
 
+// Every wave first waits for its own stores to be performed (a workgroup
+// barrier alone does not wait for global stores); then one release fence
+// per workgroup, by thread 0, makes them all visible device-wide (a fence
+// per wave cost each barrier thousands of cache write-backs).
 __device__ __forceinline__ void grid_arrive(const GridSync& gs) {
-  __threadfence();  // this thread's stores are visible device-wide
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     ChainCtl* c = gs.ctl;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     *gs.s_gen = __hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (__hip_atomic_fetch_add(&c->count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
       __hip_atomic_store(&c->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -757,7 +817,6 @@ __device__ __forceinline__ void grid_wait(const GridSync& gs) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // ---- the persistent kernel -------------------------------------------------
@@ -836,9 +895,23 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     const int kc_pad = ((klen + seg_k - 1) / seg_k) * (seg_k / 8);
     // every wave calls this once per run (the barriers protect the LDS
     // still read by the previous run, then publish the new X)
+    // The 16-wave chain kernel (kModeTiledWide) issues the first batch of X
+    // before its weight loads (its staging is on the critical path of a
+    // short launch); the verify pass measured about 1% slower that way and
+    // stages after them.  With SYNC, X is made by the previous phase, so
+    // nothing of it may be loaded before the grid barrier.
+    constexpr bool kEarlyX = MODE == kModeTiledWide && !SYNC;
+    u32x4 xpre[kStageLoads];
+    auto pre = [&]() {
+      if constexpr (kEarlyX) stage_x_load<N>(xpre, mt.x, mt.K, k0, klen, kc_pad, (int)threadIdx.x);
+    };
     auto stage = [&]() {
       sync_first();
-      stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
+      if constexpr (kEarlyX) {
+        stage_x_rest<N>(xpre, lds, mt.x, mt.K, k0, klen, kc_pad);
+      } else {
+        stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
+      }
       __syncthreads();
     };
     // tiled formats: wave w takes the w-th of nwaves equal shares of the
@@ -847,26 +920,31 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     const int64_t share0 = u + len * wave / nwaves, share1 = u + len * (wave + 1) / nwaves;
     if constexpr (MODE == kModeTiled) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchTiled, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
       else
-        tiled_run<N, kPrefetchTiled, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
     } else if constexpr (MODE == kModeTiledArgmax) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchTiled, true, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, true, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, pre, stage);
       else
-        tiled_run<N, kPrefetchTiled, false, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchTiled, false, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, pre, stage);
     } else if constexpr (MODE == kModeTiledGlu) {
+      NormBatch nb;
+      auto pre_norm = [&]() {
+        if constexpr (!SYNC) norm_first<N>(nb, mt, kc_pad);
+      };
       auto stage_norm_x = [&]() {
         sync_first();
-        stage_norm<N>(lds, mt, kc_pad, u - mt.unit0, run_end - mt.unit0, (int64_t)mt.nchunks * mt.ntiles);
+        if constexpr (SYNC) norm_first<N>(nb, mt, kc_pad);
+        stage_norm<N>(nb, lds, mt, kc_pad, u - mt.unit0, run_end - mt.unit0, (int64_t)mt.nchunks * mt.ntiles);
         __syncthreads();
       };
-      tiled_run<N, kPrefetchWide, false, kEpiGlu>(mt, chunk, share0, share1, lds, bestk, stage_norm_x);
+      tiled_run<N, kPrefetchWide, false, kEpiGlu>(mt, chunk, share0, share1, lds, bestk, pre_norm, stage_norm_x);
     } else if constexpr (MODE == kModeTiledWide) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchWide, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchWide, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
       else
-        tiled_run<N, kPrefetchWide, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, stage);
+        tiled_run<N, kPrefetchWide, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
     } else {
       // (written out rather than through stage(): a by-reference lambda on
       // this path kept the descriptor out of scalar registers and made the
@@ -876,9 +954,9 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       __syncthreads();
       auto staged = []() {};
       if (MODE == kModeMixed && mt.fmt == kFmtNvfp4Tiled) {
-        tiled_run<N, 1, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged);
+        tiled_run<N, 1, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged, staged);
       } else if (MODE == kModeMixed && mt.fmt == kFmtFp8RowTiled) {
-        tiled_run<N, 1, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged);
+        tiled_run<N, 1, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged, staged);
       } else {
         for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
           const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
