@@ -322,7 +322,9 @@ Split chain_down_split(int D, int F, int cus) {
     const int kc = (int)(ceil_div(ceil_div(F, n), sk) * sk);
     if ((int)ceil_div(F, kc) != n) continue;  // same split as a smaller n
     const int64_t units = ntiles * n;
-    const int64_t per = ceil_div(units, std::min<int64_t>(cus, units));
+    const int64_t grid = std::min<int64_t>(cus, units);
+    // per workgroup, with the chunk-aligned runs of chunk_ranges
+    const int64_t per = grid >= n ? ceil_div(ntiles, grid / n) : ceil_div(units, grid);
     const double cost = (double)std::max<int64_t>(per, 8) * (kc / sk) + 0.5 * n;
     if (cost < best_cost) {
       best_cost = cost;
@@ -367,6 +369,22 @@ ChainLayout chain_layout(int layers, int D, int F, int N, int cus) {
 // grid runs of (nearly) equal unit counts over one matrix
 void equal_ranges(int64_t units, int grid, WgRange* out) {
   for (int w = 0; w <= grid; ++w) out[w] = WgRange{units * w / grid, 0, 0};
+}
+
+// Runs that never cross a K chunk (each crossing costs a workgroup a second
+// staging and ring ramp, which in a short launch showed as a tail of late
+// workgroups): chunk c gets workgroups [c grid / C, (c + 1) grid / C) and
+// splits its tiles equally among them.  Needs grid >= nchunks.
+void chunk_ranges(int64_t ntiles, int nchunks, int grid, WgRange* out) {
+  if (grid < nchunks) {
+    equal_ranges(ntiles * nchunks, grid, out);
+    return;
+  }
+  for (int c = 0; c < nchunks; ++c) {
+    const int w0 = (int)((int64_t)c * grid / nchunks), w1 = (int)((int64_t)(c + 1) * grid / nchunks);
+    for (int w = w0; w < w1; ++w) out[w] = WgRange{c * ntiles + ntiles * (w - w0) / (w1 - w0), 0, 0};
+  }
+  out[grid] = WgRange{ntiles * nchunks, 0, 0};
 }
 
 }  // namespace
@@ -668,7 +686,7 @@ wq_status wq_mlp_chain_prepare(const wq_mlp_layer* layers, int count, int D, int
                               D, F, L.down, reinterpret_cast<char*>(part), N, 0);
   }
   equal_ranges(L.gate_up.ntiles, L.grid_gate_up, reinterpret_cast<WgRange*>(host.data() + off_rgu));
-  equal_ranges((int64_t)L.down.ntiles * L.down.nchunks, L.grid_down, reinterpret_cast<WgRange*>(host.data() + off_rdn));
+  chunk_ranges(L.down.ntiles, L.down.nchunks, L.grid_down, reinterpret_cast<WgRange*>(host.data() + off_rdn));
   if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return WQ_ERROR_LAUNCH;
