@@ -212,7 +212,9 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 constexpr int kNormLoads = 2;
 // Registers of one batch (the first one is loaded before the run's first
 // weight loads): each lane's partial sum of squares (nparts <= 64: one per
-// lane) and the h / gamma pieces p0 + j * blockDim.x, j < kNormLoads.
+// lane) and the h / gamma pieces p0 + j * blockDim.x, j < kNormLoads.  Piece
+// p is (kc, n) = (p / N, p mod N), k-major: the N lanes of one kc load the
+// same gamma piece (one request) and write consecutive LDS pieces.
 struct NormBatch {
   f32x4 h0[kNormLoads], h1[kNormLoads];
   u32x4 gm[kNormLoads];
@@ -226,7 +228,7 @@ __device__ __forceinline__ void norm_load(NormBatch& b, const DevMat& mt, int kc
 #pragma unroll
   for (int j = 0; j < kNormLoads; ++j) {
     const int p = p0 + j * (int)blockDim.x;
-    const int n = p / kc_pad, kc = p - n * kc_pad;
+    const int kc = p / N, n = p - kc * N;
     b.h0[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     b.h1[j] = b.h0[j];
     b.gm[j] = u32x4{0u, 0u, 0u, 0u};
@@ -254,7 +256,7 @@ __device__ __forceinline__ void norm_store(const NormBatch& b, char* lds, const 
   for (int j = 0; j < kNormLoads; ++j) {
     const int p = p0 + j * (int)blockDim.x;
     if (p >= total) continue;
-    const int n = p / kc_pad, kc = p - n * kc_pad;
+    const int kc = p / N, n = p - kc * N;
     const float r = rl[n];
     const float hv[8] = {b.h0[j].x, b.h0[j].y, b.h0[j].z, b.h0[j].w, b.h1[j].x, b.h1[j].y, b.h1[j].z, b.h1[j].w};
     u32x4 o = {0u, 0u, 0u, 0u};
@@ -1094,7 +1096,17 @@ __device__ __forceinline__ void chain_reduce_block(float* __restrict__ h, const 
       const int nchunks = down->nchunks;
       float acc = 0.0f;
       if (nchunks > 1) {
-        for (int c = 0; c < nchunks; ++c) acc += down->part[(size_t)c * N * D + o];
+        // eight chunks' loads in flight at a time, then added in chunk order
+        constexpr int kBatch = 8;
+        for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+          float v[kBatch];
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j)
+            v[j] = c0 + j < nchunks ? down->part[(size_t)(c0 + j) * N * D + o] : 0.0f;
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j)
+            if (c0 + j < nchunks) acc += v[j];
+        }
         acc = down->g * acc;
       } else {
         acc = down->y[o];
