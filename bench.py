@@ -48,7 +48,9 @@ PEAK_GBPS = 8000.0
 N_CYCLE = [2, 4, 8]
 NMAX = 8
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "verify_pass_traffic.txt")
-KERNEL_SOURCES = ["fp8_weight_streaming_amd/csrc/wq_kernels.hip", "fp8_weight_streaming_amd/csrc/wq_internal.h"]
+# the kernels and the planner that lays out their work (the counters belong to both)
+KERNEL_SOURCES = ["fp8_weight_streaming_amd/csrc/wq_kernels.hip", "fp8_weight_streaming_amd/csrc/wq_internal.h",
+                  "fp8_weight_streaming_amd/csrc/wq_api.cpp"]
 
 
 # ---- input generation (before the GPU is touched) ---------------------------
@@ -762,6 +764,24 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     probe_gbps = 5 * probe_buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # the same read stream with about 1% of its bytes written as scattered
+    # 256-byte write-through stores (the verify pass's outputs at N = 8 are
+    # 0.9% of its bytes): what an output byte costs in read time
+    every_kb = 96
+    wdst = torch.empty(wq.wq_probe_read_write_bytes(probe_buf.numel(), every_kb), dtype=torch.uint8, device=dev)
+    wq.wq_probe_read_write(probe_buf, wdst, every_kb, sink, stream)
+    e0.record(stream)
+    for _ in range(5):
+        wq.wq_probe_read_write(probe_buf, wdst, every_kb, sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_rw = e0.elapsed_time(e1) * 1e-3 / 5
+    t_r = probe_buf.numel() / (probe_gbps * 1e9)
+    write_probe = {"every_kb_read": every_kb, "bytes_read": probe_buf.numel(), "bytes_written": wdst.numel(),
+                   "read_only_gbps": probe_gbps, "with_writes_read_gbps": probe_buf.numel() / t_rw / 1e9,
+                   "us_per_mb_written": (t_rw - t_r) * 1e6 / (wdst.numel() / 1e6),
+                   "read_bytes_lost_per_byte_written": (t_rw - t_r) * probe_gbps * 1e9 / wdst.numel()}
+    del wdst
     copy_dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     wq.wq_probe_copy(probe_buf[: 1 << 30], copy_dst, stream)
     torch.cuda.synchronize()
@@ -811,7 +831,8 @@ def main():
                 "kernel": "wq::stream_kernel<N, tiled-NVFP4 mode> + wq::reduce_kernel (one verify pass)",
                 "avg_launch_us": kernel_s / steps * 1e6,
                 "algorithmic_bytes_per_launch_mean": total_bytes / steps,
-                "probe_read_gbps": probe_gbps, "frac_of_probe": achieved / probe_gbps}
+                "probe_read_gbps": probe_gbps, "frac_of_probe": achieved / probe_gbps,
+                "probe_write_cost": write_probe}
 
     # the plain row-major layout, timed the same way (reported only)
     plain = {}

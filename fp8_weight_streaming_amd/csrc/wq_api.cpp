@@ -58,6 +58,7 @@ struct Split {
   int kc = 0;
   int nchunks = 0;
   int ntiles = 0;
+  int tb = 0;  // tiles per block of a blocked split (all-tiled verify passes), else 0
 };
 
 int seg_k(int fmt) {
@@ -147,7 +148,7 @@ wq_status check_ptrs(int fmt, const void* w, const void* s, const void* x, const
 
 // Workspace bytes of the split-K scratch (chunk partial sums) of one matrix.
 size_t split_scratch_bytes(const Split& s, int M, int N) {
-  if (s.nchunks <= 1) return 0;
+  if (s.nchunks <= 1 || s.tb > 0) return 0;
   return align_up((size_t)s.nchunks * N * M * sizeof(float), kAlign);
 }
 
@@ -167,7 +168,8 @@ DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x
   d.nchunks = sp.nchunks;
   d.ntiles = sp.ntiles;
   d.unit0 = unit0;
-  if (sp.nchunks > 1) d.part = reinterpret_cast<float*>(scratch);
+  d.tb = sp.tb;
+  if (sp.nchunks > 1 && sp.tb == 0) d.part = reinterpret_cast<float*>(scratch);
   return d;
 }
 
@@ -198,14 +200,19 @@ wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x
 }
 
 // ---- verify pass layout ------------------------------------------------------
+// The pass's matrices in the order of the unit list (and of the device
+// table): large split matrices computed in blocks first, then the rest, each
+// in the caller's order.  Every per-matrix array below is in this order.
 struct PassLayout {
+  std::vector<wq_matrix> descs;
   std::vector<Split> splits;
   std::vector<size_t> scratch_off;
   std::vector<ReduceTask> tasks;  // reduction runs of the split matrices
   size_t table_bytes = 0, ranges_bytes = 0, tasks_bytes = 0, scratch_bytes = 0, total = 0;
   int grid = 0;
   int64_t units = 0;
-  int64_t dyn_chunks = 0;  // upper bound, for sizing (the tail holds at most all units)
+  int64_t dyn_chunks = 0;  // upper bound on the tail's claim entries, for sizing
+  uint32_t lds_extra = 0;  // LDS for blocked chunk sums
 };
 
 wq_status check_descs(const wq_matrix* descs, int count, int N) {
@@ -220,31 +227,78 @@ wq_status check_descs(const wq_matrix* descs, int count, int N) {
   return WQ_SUCCESS;
 }
 
-PassLayout pass_layout(const wq_matrix* descs, int count, int N, int cus) {
+bool all_tiled(const wq_matrix* descs, int count) {
+  for (int i = 0; i < count; ++i)
+    if (!is_tiled(descs[i].fmt)) return false;
+  return true;
+}
+
+// Balancing cost of one unit (16 rows of K chunk c): its weight bytes plus a
+// fixed per-unit overhead.
+double unit_cost(const wq_matrix& d, const Split& sp, int c) {
+  const int klen = std::min(sp.kc, d.K - c * sp.kc);
+  const double bytes_per_k = is_nvfp4(d.fmt) ? 16.0 * 0.5625 : 16.0;
+  return bytes_per_k * klen + 4096.0;
+}
+double tile_cost(const wq_matrix& d, const Split& sp) {
+  double t = 0.0;
+  for (int c = 0; c < sp.nchunks; ++c) t += unit_cost(d, sp, c);
+  return t;
+}
+
+// A split matrix of an all-tiled pass is blocked when an average
+// workgroup's share of the pass holds at least this many of its tiles:
+// each block costs a restaging of X per chunk, which smaller shares (a
+// single decode layer, say) do not amortize; they keep the reduction.
+constexpr double kBlockMinTiles = 32.0;
+
+PassLayout pass_layout(const wq_matrix* in, int count, int N, int cus) {
   PassLayout L;
-  L.splits.resize(count);
-  L.scratch_off.resize(count);
+  std::vector<Split> sp(count);
+  double total = 0.0;
   for (int i = 0; i < count; ++i) {
-    L.splits[i] = verify_split(descs[i].fmt, descs[i].M, descs[i].K);
-    L.units += (int64_t)L.splits[i].nchunks * L.splits[i].ntiles;
+    sp[i] = verify_split(in[i].fmt, in[i].M, in[i].K);
+    total += tile_cost(in[i], sp[i]) * sp[i].ntiles;
+    L.units += (int64_t)sp[i].nchunks * sp[i].ntiles;
   }
   L.grid = (int)std::min<int64_t>(cus, L.units);
+  const double share = total / L.grid;
+  const bool tiled = all_tiled(in, count);
+  std::vector<char> blk(count, 0);
+  for (int i = 0; i < count; ++i)
+    blk[i] = tiled && sp[i].nchunks > 1 && share >= kBlockMinTiles * tile_cost(in[i], sp[i]);
+  int64_t blocked_tiles = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int i = 0; i < count; ++i) {
+      if (blk[i] != (pass == 0)) continue;
+      L.descs.push_back(in[i]);
+      L.splits.push_back(sp[i]);
+      if (blk[i]) {
+        L.splits.back().tb = part_tiles_for(N);
+        L.lds_extra = (uint32_t)part_tiles_for(N) * kPartTileBytes;
+        blocked_tiles += sp[i].ntiles;
+      }
+    }
+  L.scratch_off.resize(count);
   for (int i = 0; i < count; ++i) {
-    if (L.splits[i].nchunks <= 1) continue;
-    const int64_t outs = (int64_t)N * descs[i].M;
+    if (L.splits[i].nchunks <= 1 || L.splits[i].tb > 0) continue;
+    const int64_t outs = (int64_t)N * L.descs[i].M;
     for (int64_t b = 0; b < outs; b += kReduceRun)
       L.tasks.push_back(ReduceTask{b, i, (int32_t)std::min<int64_t>(kReduceRun, outs - b)});
   }
   L.table_bytes = align_up((size_t)count * sizeof(DevMat), kAlign);
-  L.dyn_chunks = ceil_div(L.units, kDynChunkMin);
+  // claims: at most one per kDynChunkMin units, or per tile of a blocked
+  // matrix, plus one per matrix (a claim may end at a matrix's end), plus
+  // the end entry
+  L.dyn_chunks = ceil_div(L.units, kDynChunkMin) + blocked_tiles + count + 1;
   L.ranges_bytes = align_up((size_t)(L.grid + 1) * sizeof(WgRange) + sizeof(DynSched) +
-                                (size_t)L.dyn_chunks * sizeof(int32_t),
+                                (size_t)L.dyn_chunks * sizeof(DynClaim),
                             kAlign);
   L.tasks_bytes = align_up(L.tasks.size() * sizeof(ReduceTask), kAlign);
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     L.scratch_off[i] = off;
-    off += split_scratch_bytes(L.splits[i], descs[i].M, N);
+    off += split_scratch_bytes(L.splits[i], L.descs[i].M, N);
   }
   L.scratch_bytes = off;
   L.total = L.table_bytes + L.ranges_bytes + L.tasks_bytes + L.scratch_bytes;
@@ -266,12 +320,7 @@ int dyn_chunk_units(int64_t units, int grid) {
 // ramp up per unit, measured slower with one).
 std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout& L, bool tiled_only,
                              int64_t* dyn_begin) {
-  auto unit_cost = [&](int i, int c) {
-    const Split& sp = L.splits[i];
-    const int klen = std::min(sp.kc, descs[i].K - c * sp.kc);
-    const double bytes_per_k = is_nvfp4(descs[i].fmt) ? 16.0 * 0.5625 : 16.0;
-    return bytes_per_k * klen + 4096.0;
-  };
+  auto unit_cost = [&](int i, int c) { return wq::unit_cost(descs[i], L.splits[i], c); };
   double total = 0.0;
   for (int i = 0; i < count; ++i)
     for (int c = 0; c < L.splits[i].nchunks; ++c) total += unit_cost(i, c) * L.splits[i].ntiles;
@@ -284,6 +333,23 @@ std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout
   const int last = tail ? L.grid : L.grid - 1;  // with a tail, range grid's end is a boundary too
   for (int i = 0; i < count; ++i) {
     const Split& sp = L.splits[i];
+    if (sp.tb > 0) {
+      // blocked split: units are tile-major and a range holds whole tiles
+      // (every chunk of a tile runs in one workgroup)
+      double tile_cost = 0.0;
+      for (int c = 0; c < sp.nchunks; ++c) tile_cost += unit_cost(i, c);
+      const double end = acc + tile_cost * sp.ntiles;
+      while (w <= last && stat * w / L.grid < end) {
+        const double need = (stat * w / L.grid - acc) / tile_cost;
+        int64_t j = need <= 0.0 ? 0 : (int64_t)std::ceil(need);
+        if (j > sp.ntiles) j = sp.ntiles;
+        ranges[w] = WgRange{u + j * sp.nchunks, i, 0};
+        ++w;
+      }
+      acc = end;
+      u += (int64_t)sp.nchunks * sp.ntiles;
+      continue;
+    }
     for (int c = 0; c < sp.nchunks; ++c) {
       const double uc = unit_cost(i, c);
       const double end = acc + uc * sp.ntiles;
@@ -302,6 +368,60 @@ std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout
   ranges[0] = WgRange{0, 0, 0};
   *dyn_begin = ranges[L.grid].begin;
   return ranges;
+}
+
+// The dynamic tail [dyn_begin, units) as claims, each followed by the next
+// one's begin (the last entry only ends the tail): `chunk` units, rounded up
+// to whole tiles where a claim ends inside a blocked matrix (whose units are
+// tile-major); a claim starting in a blocked matrix takes chunk / nchunks
+// tiles of it (at least one).
+std::vector<DynClaim> tail_claims(const std::vector<DevMat>& mats, const PassLayout& L, int64_t dyn_begin,
+                                  int chunk) {
+  const int count = (int)mats.size();
+  auto units_of = [&](int j) { return (int64_t)L.splits[j].nchunks * L.splits[j].ntiles; };
+  auto tile_end = [&](int j, int64_t v) {  // first tile boundary of matrix j at or after unit v
+    const int64_t nc = L.splits[j].nchunks;
+    return mats[j].unit0 + std::min(ceil_div(v - mats[j].unit0, nc) * nc, units_of(j));
+  };
+  std::vector<DynClaim> claims;
+  int i = 0;
+  for (int64_t u = dyn_begin; u < L.units;) {
+    while (i + 1 < count && mats[i + 1].unit0 <= u) ++i;
+    int64_t e;
+    if (L.splits[i].tb > 0) {
+      const int64_t tiles = std::max<int64_t>(1, chunk / L.splits[i].nchunks);
+      e = tile_end(i, u + tiles * L.splits[i].nchunks);
+    } else {
+      e = std::min<int64_t>(u + chunk, L.units);
+      int j = i;  // the matrix holding unit e - 1
+      while (j + 1 < count && mats[j + 1].unit0 < e) ++j;
+      if (L.splits[j].tb > 0) e = tile_end(j, e);
+    }
+    claims.push_back(DynClaim{u, i, 0});
+    u = e;
+  }
+  claims.push_back(DynClaim{L.units, count - 1, 0});
+  return claims;
+}
+
+// Every static range and every claim starts at a tile boundary of any
+// blocked matrix it starts in (what the kernel relies on).
+bool blocks_whole(const std::vector<DevMat>& mats, const PassLayout& L, const std::vector<WgRange>& ranges,
+                  const std::vector<DynClaim>& claims) {
+  // v is in matrix j, or is the first unit after it
+  auto whole = [&](int64_t v, int j) {
+    if (j < 0 || j >= (int)mats.size()) return false;
+    const int64_t local = v - mats[j].unit0;
+    const int64_t units = (int64_t)L.splits[j].nchunks * L.splits[j].ntiles;
+    if (local < 0 || local > units) return false;
+    if (L.splits[j].tb == 0 || local == units) return true;
+    return local % L.splits[j].nchunks == 0;
+  };
+  for (size_t w = 0; w + 1 < ranges.size(); ++w)
+    if (!whole(ranges[w].begin, ranges[w].mat)) return false;
+  for (const DynClaim& c : claims)
+    if (!whole(c.begin, c.mat)) return false;
+  return true;
 }
 
 // ---- chained MLP layers --------------------------------------------------------
@@ -514,7 +634,7 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
   int64_t unit0 = 0;
   bool any_nv = false, any_fp8 = false, any_tiled = false, all_aligned = true;
   for (int i = 0; i < count; ++i) {
-    const wq_matrix& d = descs[i];
+    const wq_matrix& d = L.descs[i];
     mats[i] = dev_mat(d.fmt, d.w, d.scales, d.global_scale, d.x, d.y, d.M, d.K, L.splits[i],
                       scratch + L.scratch_off[i], N, unit0);
     unit0 += (int64_t)L.splits[i].nchunks * L.splits[i].ntiles;
@@ -528,7 +648,8 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
     }
   }
   int64_t dyn_begin = L.units;
-  const std::vector<WgRange> ranges = balance(descs, count, L, any_tiled && !any_nv && !any_fp8, &dyn_begin);
+  const std::vector<WgRange> ranges =
+      balance(L.descs.data(), count, L, any_tiled && !any_nv && !any_fp8, &dyn_begin);
   std::memcpy(host.data(), mats.data(), sizeof(DevMat) * count);
   std::memcpy(host.data() + L.table_bytes, ranges.data(), sizeof(WgRange) * ranges.size());
   // the dynamic tail: its bounds, zeroed counters and each chunk's matrix
@@ -536,18 +657,12 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
   dyn.begin = dyn_begin;
   dyn.end = L.units;
   dyn.chunk = dyn_chunk_units(L.units, L.grid);
-  dyn.count = (int32_t)ceil_div(L.units - dyn_begin, dyn.chunk);
+  const std::vector<DynClaim> claims = tail_claims(mats, L, dyn_begin, dyn.chunk);
+  if ((int64_t)claims.size() > L.dyn_chunks || !blocks_whole(mats, L, ranges, claims)) return WQ_ERROR_INVALID_VALUE;
+  dyn.count = (int32_t)claims.size() - 1;
   char* dyn_host = host.data() + L.table_bytes + sizeof(WgRange) * ranges.size();
   std::memcpy(dyn_host, &dyn, sizeof(DynSched));
-  {
-    int32_t* cm = reinterpret_cast<int32_t*>(dyn_host + sizeof(DynSched));
-    int i = 0;
-    for (int32_t k = 0; k < dyn.count; ++k) {
-      const int64_t u0 = dyn_begin + (int64_t)k * dyn.chunk;
-      while (i + 1 < count && mats[i + 1].unit0 <= u0) ++i;
-      cm[k] = i;
-    }
-  }
+  std::memcpy(dyn_host + sizeof(DynSched), claims.data(), sizeof(DynClaim) * claims.size());
   if (!L.tasks.empty())
     std::memcpy(host.data() + L.table_bytes + L.ranges_bytes, L.tasks.data(), sizeof(ReduceTask) * L.tasks.size());
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -566,20 +681,30 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
   plan->ranges_offset = L.table_bytes;
   plan->reduce_offset = L.table_bytes + L.ranges_bytes;
   plan->reduce_runs = (int32_t)L.tasks.size();
+  plan->lds_extra = (int32_t)L.lds_extra;
   return WQ_SUCCESS;
+}
+
+// LDS past the X chunk and the zero block: the blocked chunk sums of an
+// all-tiled pass, or nothing
+static bool lds_extra_ok(const wq_verify_plan& p) {
+  return p.lds_extra == 0 ||
+         (p.mode == kModeTiled && p.lds_extra > 0 && p.lds_extra % kPartTileBytes == 0 &&
+          lds_bytes_for(p.N) + (uint32_t)p.lds_extra <= kLdsLimit);
 }
 
 wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {
   if (!plan || !plan->workspace || plan->N < 1 || plan->N > 8 || plan->grid < 1 || plan->count < 1 ||
       plan->mode < kModeNvfp4Aligned || plan->mode > kModeTiled || plan->ranges_offset >= plan->workspace_bytes ||
-      plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes))
+      plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes) ||
+      !lds_extra_ok(*plan))
     return WQ_ERROR_INVALID_VALUE;
   const char* ws = static_cast<const char*>(plan->workspace);
   const DevMat none{};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_stream(plan->N, plan->mode, reinterpret_cast<const DevMat*>(ws),
                                reinterpret_cast<const WgRange*>(ws + plan->ranges_offset), none, plan->grid,
-                               lds_bytes_for(plan->N), s);
+                               lds_bytes_for(plan->N) + (size_t)plan->lds_extra, s);
   if (e == hipSuccess && plan->reduce_runs > 0)
     e = launch_reduce(reinterpret_cast<const DevMat*>(ws), reinterpret_cast<const ReduceTask*>(ws + plan->reduce_offset),
                       none, plan->reduce_runs, plan->N, s);
@@ -589,13 +714,15 @@ wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {
 wq_status wq_verify_launch_n(const wq_verify_plan* plan, const int32_t* n_device, void* stream) {
   if (!plan || !plan->workspace || !n_device || ((uintptr_t)n_device & 3u) || plan->N != 8 || plan->grid < 1 ||
       plan->count < 1 || plan->mode != kModeTiled || plan->ranges_offset >= plan->workspace_bytes ||
-      plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes))
+      plan->reduce_runs < 0 || (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes) ||
+      !lds_extra_ok(*plan))
     return WQ_ERROR_INVALID_VALUE;
   const char* ws = static_cast<const char*>(plan->workspace);
   const DevMat none{};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_stream_dyn(reinterpret_cast<const DevMat*>(ws),
-                                   reinterpret_cast<const WgRange*>(ws + plan->ranges_offset), n_device, plan->grid, s);
+                                   reinterpret_cast<const WgRange*>(ws + plan->ranges_offset), n_device, plan->grid,
+                                   lds_bytes_for(8) + (size_t)plan->lds_extra, s);
   if (e == hipSuccess && plan->reduce_runs > 0)
     e = launch_reduce(reinterpret_cast<const DevMat*>(ws), reinterpret_cast<const ReduceTask*>(ws + plan->reduce_offset),
                       none, plan->reduce_runs, 8, s, n_device);

@@ -53,7 +53,26 @@ constexpr uint32_t lds_bytes_for(int n) { return (uint32_t)kKcMax * 2u * n + 512
 // Head acceptance (kModeTiledArgmax) adds, past the zero block, each wave's
 // best keys: 8 waves x 8 columns x 8 bytes.
 constexpr uint32_t kArgLdsBytes = 512;
-constexpr uint32_t kMaxLdsBytes = lds_bytes_for(8) + kArgLdsBytes;
+// LDS per workgroup on gfx950 (160 KB), less what the kernels declare
+// statically (at most 32 bytes): the most dynamic LDS a launch may ask for.
+constexpr uint32_t kLdsLimit = 160u * 1024u - 256u;
+// A large split matrix of an all-tiled verify pass is processed in blocks of
+// tiles: one workgroup computes every K chunk of a block in turn and keeps
+// the block's chunk sums in LDS past the zero block (32 lanes x 4 floats per
+// tile), so no partial sums leave the CU and no reduction launch follows.
+// A block holds as many tiles as the LDS left at N allows (40 at N = 8).
+constexpr uint32_t kPartTileBytes = 512;
+constexpr int kPartTilesMax = 256;
+constexpr int part_tiles_for(int n) {
+  return (int)((kLdsLimit - lds_bytes_for(n)) / kPartTileBytes) < kPartTilesMax
+             ? (int)((kLdsLimit - lds_bytes_for(n)) / kPartTileBytes)
+             : kPartTilesMax;
+}
+template <int N>
+__host__ __device__ constexpr uint32_t kPartOffset() { return kZeroOffset<N>() + kZeroBytes<N>(); }
+constexpr uint32_t kMaxLdsBytes = kLdsLimit;
+static_assert(lds_bytes_for(8) + kArgLdsBytes <= kLdsLimit, "LDS budget exceeded");
+static_assert(part_tiles_for(8) >= 32, "too few tiles per block at N = 8");
 // idle-lane reads: tiled NVFP4 at 256N + 192N + 16, plain NVFP4 at 192N + 16,
 // FP8-row at 16N + 16 bytes past the zero block's start
 static_assert(kZeroBytes<1>() >= 448u * 1 + 16u && kZeroBytes<8>() >= 448u * 8 + 16u, "zero block too small");
@@ -89,7 +108,11 @@ struct DevMat {
   float g2;
   float eps;
   int nparts;
-  int pad;
+  // Blocked split (large split matrices of all-tiled verify passes): tiles
+  // per block, else 0.  The matrix's units are then tile-major (unit =
+  // tile * nchunks + chunk), a workgroup's range holds whole tiles, and the
+  // workgroup takes them tb at a time, every chunk of such a block in turn.
+  int tb;
 };
 
 // First unit (and the matrix holding it) of each workgroup's run.
@@ -100,19 +123,26 @@ struct WgRange {
 };
 
 // The dynamic tail of a verify pass, stored right after the grid + 1
-// ranges: units [begin, end) are handed out in chunks of `chunk` units, in
-// order, to whichever workgroup asks next (an atomic counter), so that
-// workgroups that streamed their static range faster take more.  `next`
-// and `done` start at 0 (the plan's upload zeroes them); the last
-// workgroup to finish a launch sets them back to 0.  `chunk_mat` (count
-// entries) follows: the matrix holding each chunk's first unit.
+// ranges: units [begin, end) are handed out as `count` claims, in order, to
+// whichever workgroup asks next (an atomic counter), so that workgroups
+// that streamed their static range faster take more.  `next` and `done`
+// start at 0 (the plan's upload zeroes them); the last workgroup to finish a
+// launch sets them back to 0.  The claims follow (count + 1 entries, the
+// last one only ending the one before): claim i is units
+// [claims[i].begin, claims[i + 1].begin), whose first unit is in matrix
+// claims[i].mat.
 struct DynSched {
   int64_t begin;
   int64_t end;
-  int32_t chunk;
+  int32_t chunk;  // units per claim outside blocked matrices
   int32_t count;
   uint32_t next;
   uint32_t done;
+};
+struct DynClaim {
+  int64_t begin;
+  int32_t mat;
+  int32_t pad;
 };
 // Share of a pass's cost left to the dynamic tail, and its chunk sizes:
 // units per workgroup / 32, within [8, 16] (16 for the dense 64-layer
@@ -176,7 +206,7 @@ hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevM
                          hipStream_t stream, const int32_t* n_dev = nullptr);
 // the tiled verify pass with N read from n_dev (a plan prepared for N = 8)
 hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const int32_t* n_dev, int grid,
-                             hipStream_t stream);
+                             size_t lds_bytes, hipStream_t stream);
 // h[n][m] += the down product of `down` (a device-side descriptor: its
 // chunk partial sums in chunk order, times g; or its y for one chunk),
 // then ssp[n][p] = sum of h[n][m]^2 over block p's outputs.  down == null:

@@ -483,9 +483,15 @@ __device__ __forceinline__ uint64_t greedy_key(float v, int m) {
 constexpr int kEpiStore = 0;
 constexpr int kEpiArgmax = 1;
 constexpr int kEpiGlu = 2;
-template <int N, int PF, bool FP8, int EPI, typename Pre, typename Stage>
-__device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, const char* lds,
-                          uint64_t* bestk, Pre&& pre, Stage&& stage) {
+// Units [first, end) are tiles first - ubase .. end - 1 - ubase of chunk
+// `chunk`.  ptile0 >= 0 marks a blocked split matrix (DevMat::tb) whose
+// block starts at tile ptile0 (BLK kernels only): the chunk sums of the
+// block's tiles wait in LDS (one 512-byte slot per tile of the block) for
+// the next chunk, which adds its own to them, in chunk order as
+// reduce_kernel does, and the last chunk stores y.
+template <int N, int PF, bool FP8, int EPI, bool BLK, typename Pre, typename Stage>
+__device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, int64_t ubase, int ptile0,
+                          char* lds, uint64_t* bestk, Pre&& pre, Stage&& stage) {
   pre();
   if (first >= end) {
     stage();
@@ -499,7 +505,7 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
   const int klen = min(mt.kc, mt.K - k0);
   const int nst = (klen + kStep - 1) / kStep;
   const int cnt = (int)(end - first);
-  const int tile0 = (int)((first - mt.unit0) - (int64_t)chunk * mt.ntiles);
+  const int tile0 = (int)(first - ubase);
   const uint32_t steps_per_row = (uint32_t)((mt.K + kStep - 1) / kStep);
   const uint32_t base_step = (uint32_t)(k0 / kStep);
   const uint64_t total = (uint64_t)mt.ntiles * steps_per_row * kBlock;  // < 2^32 (checked on the host)
@@ -585,7 +591,12 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
   // compiler's vmcnt waits exact across the epilogue (a conditional store
   // makes it wait for everything).
   constexpr int kStores = N < 4 ? N : 4;
-  const bool split = mt.nchunks > 1;
+  const bool blocked = BLK && ptile0 >= 0;
+  const bool split = mt.nchunks > 1 && !blocked;
+  // blocked: chunk sums come from (after the first chunk) and go to (before
+  // the last) the block's LDS slots; only the last chunk stores
+  const bool from_lds = blocked && chunk > 0;
+  const bool to_lds = blocked && chunk < mt.nchunks - 1;
   float* const obase = split ? mt.part + (size_t)chunk * N * mt.M : mt.y;
   // (no output buffer -- head acceptance without logits -- drops every store)
   const int F = mt.M / 2;  // kEpiGlu: outputs per column
@@ -637,6 +648,11 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       const bool half_ok = (lane & 16) ? odd : (!odd || ci > 0);
       // the FP8 row scale of the lane's row (m = 16 t + c); 1 for partials
       const float rscale = split ? 1.0f : __uint_as_float(rv[slot]);
+      // blocked: lane l and l + 32 hold the same (n, m), so both read the
+      // slot of lane l % 32; lanes 0..31 write it
+      f32x4 pin = {0.f, 0.f, 0.f, 0.f}, pout;
+      const uint32_t poff = kPartOffset<N>() + (uint32_t)(((tile0 + ci - ptile0) * 32 + (lane & 31)) * 16);
+      if (from_lds) pin = *reinterpret_cast<const f32x4*>(lds + poff);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // the swap gives every lane the low half's value (.x) and the high
@@ -645,8 +661,16 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
         // same sum.  FP8: lanes 0..31 hold rows n < 8 (the upper half holds
         // rows 8..15, which are zero), copied to both halves.
         const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
-        const float cur = FP8 ? rscale * __uint_as_float(p.x)
-                              : gscale * (__uint_as_float(p.x) + __uint_as_float(p.y));
+        float cur;
+        if (blocked) {
+          // the running sum over chunks: 0 + s_0 + s_1 + ..., in that order
+          const float sc = FP8 ? __uint_as_float(p.x) : __uint_as_float(p.x) + __uint_as_float(p.y);
+          const float run = pin[r] + sc;
+          pout[r] = run;
+          cur = FP8 ? rscale * run : gscale * run;
+        } else {
+          cur = FP8 ? rscale * __uint_as_float(p.x) : gscale * (__uint_as_float(p.x) + __uint_as_float(p.y));
+        }
         acc[r] = 0.f;
         // sums sit at lane 16 * (n / 4) + m % 16 (and again 32 lanes up):
         // the 16-lane swap brings the even tile to rows 0 and 2 and the odd
@@ -662,9 +686,10 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
           bestk[r] = key > bestk[r] ? key : bestk[r];
         }
         const int n = r + 4 * (lane >> 5);
-        const bool live = emit && half_ok && m < mt.M && n < N;
+        const bool live = emit && half_ok && m < mt.M && n < N && !to_lds;
         so[r] = live ? (uint32_t)((n * mt.M + m) * 4) : kDropOffset;
       }
+      if (to_lds && lane < 32) *reinterpret_cast<f32x4*>(lds + poff) = pout;
     }
 #pragma unroll
     for (int r = 0; r < kStores; ++r) {
@@ -823,7 +848,8 @@ __device__ __forceinline__ void grid_wait(const GridSync& gs) {
 
 // ---- the persistent kernel -------------------------------------------------
 // Workgroup w processes units [range[w].begin, range[w+1].begin) of the
-// global unit list (matrix-major, then chunk, then tile).  For a single
+// global unit list (matrix-major, then chunk, then tile; then tile, then
+// chunk for a blocked split).  For a single
 // matrix (mats == nullptr) the split is computed here, equal by units.
 // SYNC (the single-launch chain, one matrix, no ranges table: equal
 // shares): the first staging of the call first waits at the grid barrier
@@ -865,6 +891,7 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
                             : nullptr;
   __shared__ uint32_t s_claim;
   bool waited = false;
+  int bchunk = 0;  // blocked split: the next chunk of the current block
   // the barrier at the start of a staging (protects the LDS still read by
   // the previous run; with SYNC the first one is the grid barrier)
   auto sync_first = [&]() {
@@ -884,8 +911,33 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     const int64_t mend = mt.unit0 + (int64_t)mt.nchunks * mt.ntiles;
     if (u >= mend) { ++mi; continue; }
     const int64_t local = u - mt.unit0;
-    const int chunk = (int)(local / mt.ntiles);
-    const int64_t run_end = min(u_end, mt.unit0 + (int64_t)(chunk + 1) * mt.ntiles);
+    // The segment: units [first, run_end) of one K chunk, tile = unit - ubase.
+    // A blocked split's units are tile-major (tile * nchunks + chunk) and a
+    // range holds whole tiles: the run takes them mt.tb at a time, all chunks
+    // of such a block in turn (bchunk counts them), and moves u past the
+    // block after its last chunk.
+    int chunk, ptile0 = -1;
+    int64_t first, run_end, ubase;
+    if (mt.tb > 0) {
+      const int nc = mt.nchunks;
+      const int t0 = (int)(local / nc);
+      const int t1 = min(t0 + mt.tb, (int)((min(u_end, mend) - mt.unit0) / nc));
+      chunk = bchunk;
+      first = t0;
+      run_end = t1;
+      ubase = 0;
+      ptile0 = t0;
+      if (++bchunk == nc) {
+        bchunk = 0;
+        u = mt.unit0 + (int64_t)t1 * nc;
+      }
+    } else {
+      chunk = (int)(local / mt.ntiles);
+      ubase = mt.unit0 + (int64_t)chunk * mt.ntiles;
+      first = u;
+      run_end = min(u_end, ubase + mt.ntiles);
+      u = run_end;
+    }
     const int k0 = chunk * mt.kc;
     const int klen = min(mt.kc, mt.K - k0);
     // X is staged (zero-padded) to whole steps of the format, which every
@@ -918,18 +970,22 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     };
     // tiled formats: wave w takes the w-th of nwaves equal shares of the
     // run's consecutive tiles
-    const int64_t len = run_end - u;
-    const int64_t share0 = u + len * wave / nwaves, share1 = u + len * (wave + 1) / nwaves;
+    const int64_t len = run_end - first;
+    const int64_t share0 = first + len * wave / nwaves, share1 = first + len * (wave + 1) / nwaves;
     if constexpr (MODE == kModeTiled) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchTiled, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
+        tiled_run<N, kPrefetchTiled, true, kEpiStore, true>(mt, chunk, share0, share1, ubase, ptile0, lds, bestk, pre,
+                                                             stage);
       else
-        tiled_run<N, kPrefetchTiled, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
+        tiled_run<N, kPrefetchTiled, false, kEpiStore, true>(mt, chunk, share0, share1, ubase, ptile0, lds, bestk, pre,
+                                                              stage);
     } else if constexpr (MODE == kModeTiledArgmax) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchTiled, true, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, pre, stage);
+        tiled_run<N, kPrefetchTiled, true, kEpiArgmax, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, pre,
+                                                               stage);
       else
-        tiled_run<N, kPrefetchTiled, false, kEpiArgmax>(mt, chunk, share0, share1, lds, bestk, pre, stage);
+        tiled_run<N, kPrefetchTiled, false, kEpiArgmax, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, pre,
+                                                                stage);
     } else if constexpr (MODE == kModeTiledGlu) {
       NormBatch nb;
       auto pre_norm = [&]() {
@@ -938,15 +994,16 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       auto stage_norm_x = [&]() {
         sync_first();
         if constexpr (SYNC) norm_first<N>(nb, mt, kc_pad);
-        stage_norm<N>(nb, lds, mt, kc_pad, u - mt.unit0, run_end - mt.unit0, (int64_t)mt.nchunks * mt.ntiles);
+        stage_norm<N>(nb, lds, mt, kc_pad, first - mt.unit0, run_end - mt.unit0, (int64_t)mt.nchunks * mt.ntiles);
         __syncthreads();
       };
-      tiled_run<N, kPrefetchWide, false, kEpiGlu>(mt, chunk, share0, share1, lds, bestk, pre_norm, stage_norm_x);
+      tiled_run<N, kPrefetchWide, false, kEpiGlu, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, pre_norm,
+                                                  stage_norm_x);
     } else if constexpr (MODE == kModeTiledWide) {
       if (mt.fmt == kFmtFp8RowTiled)
-        tiled_run<N, kPrefetchWide, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
+        tiled_run<N, kPrefetchWide, true, kEpiStore, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, pre, stage);
       else
-        tiled_run<N, kPrefetchWide, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, pre, stage);
+        tiled_run<N, kPrefetchWide, false, kEpiStore, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, pre, stage);
     } else {
       // (written out rather than through stage(): a by-reference lambda on
       // this path kept the descriptor out of scalar registers and made the
@@ -956,12 +1013,12 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       __syncthreads();
       auto staged = []() {};
       if (MODE == kModeMixed && mt.fmt == kFmtNvfp4Tiled) {
-        tiled_run<N, 1, false, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged, staged);
+        tiled_run<N, 1, false, kEpiStore, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, staged, staged);
       } else if (MODE == kModeMixed && mt.fmt == kFmtFp8RowTiled) {
-        tiled_run<N, 1, true, kEpiStore>(mt, chunk, share0, share1, lds, bestk, staged, staged);
+        tiled_run<N, 1, true, kEpiStore, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, staged, staged);
       } else {
-        for (int64_t uu = u + wave; uu < run_end; uu += nwaves) {
-          const int tile = (int)((uu - mt.unit0) - (int64_t)chunk * mt.ntiles);
+        for (int64_t uu = first + wave; uu < run_end; uu += nwaves) {
+          const int tile = (int)(uu - ubase);
           if constexpr (MODE == kModeNvfp4Aligned) {
             nvfp4_unit<N, kPrefetch, true>(mt, chunk, tile, lds);
           } else if constexpr (MODE == kModeNvfp4) {
@@ -977,7 +1034,6 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
         }
       }
     }
-    u = run_end;
   }
   if (!dyn) break;
   __syncthreads();  // every wave has read the previous claim
@@ -985,9 +1041,10 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
   __syncthreads();
   const uint32_t idx = s_claim;
   if (idx >= (uint32_t)dyn->count) break;
-  u = dyn->begin + (int64_t)idx * dyn->chunk;
-  u_end = min(u + (int64_t)dyn->chunk, dyn->end);
-  mi = reinterpret_cast<const int32_t*>(dyn + 1)[idx];
+  const DynClaim* const claims = reinterpret_cast<const DynClaim*>(dyn + 1);
+  u = claims[idx].begin;
+  u_end = claims[idx + 1].begin;
+  mi = claims[idx].mat;
   }
   if constexpr (SYNC) {
     if (!waited) grid_wait(*gs);
@@ -1226,12 +1283,11 @@ static hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done) {
 }
 
 hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const int32_t* n_dev, int grid,
-                             hipStream_t stream) {
+                             size_t lds_bytes, hipStream_t stream) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = allow_lds(reinterpret_cast<const void*>(&stream_kernel_dyn), lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(stream_kernel_dyn, dim3(grid), dim3(kThreadsTiled), lds_bytes_for(8), stream, mats, ranges,
-                     n_dev);
+  hipLaunchKernelGGL(stream_kernel_dyn, dim3(grid), dim3(kThreadsTiled), lds_bytes, stream, mats, ranges, n_dev);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ class WqVerifyPlan(ctypes.Structure):
     _fields_ = [("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("count", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("mode", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("ranges_offset", ctypes.c_size_t), ("reduce_offset", ctypes.c_size_t),
-                ("reduce_runs", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("reduce_runs", ctypes.c_int32), ("lds_extra", ctypes.c_int32)]
 
 
 class WqMlpLayer(ctypes.Structure):
@@ -102,6 +102,10 @@ _lib.wq_probe_read.restype = _I
 _lib.wq_probe_read.argtypes = [_P, _S, _P, _P]
 _lib.wq_probe_copy.restype = _I
 _lib.wq_probe_copy.argtypes = [_P, _P, _S, _P]
+_lib.wq_probe_read_write_bytes.restype = _S
+_lib.wq_probe_read_write_bytes.argtypes = [_S, _I]
+_lib.wq_probe_read_write.restype = _I
+_lib.wq_probe_read_write.argtypes = [_P, _S, _P, _I, _P, _P]
 
 _lib.wq_nvfp4_tiled_bytes.restype = _S
 _lib.wq_nvfp4_tiled_bytes.argtypes = [_I, _I]
@@ -149,7 +153,8 @@ EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm
             "wq_verify_launch_n", "wq_nvfp4_tile_glu", "wq_mlp_chain_workspace_bytes", "wq_mlp_chain_split",
             "wq_mlp_chain_prepare", "wq_mlp_chain_launch", "wq_mlp_chain_launch_persistent",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
-            "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy"]
+            "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy", "wq_probe_read_write_bytes",
+            "wq_probe_read_write"]
 
 
 def lib() -> ctypes.CDLL:
@@ -318,6 +323,17 @@ def wq_probe_read(src, sink, stream=None, nbytes: Optional[int] = None):
     """Stream `src` (device tensor) once with the weight stream's loads."""
     nb = _nbytes(src) if nbytes is None else nbytes
     _check(_lib.wq_probe_read(_ptr(src), nb, _ptr(sink), _stream(stream)), "wq_probe_read")
+
+
+def wq_probe_read_write_bytes(nbytes: int, every_kb: int) -> int:
+    return int(_lib.wq_probe_read_write_bytes(nbytes, every_kb))
+
+
+def wq_probe_read_write(src, dst, every_kb: int, sink, stream=None, nbytes: Optional[int] = None):
+    """Stream `src` once, writing 256 bytes per wave to `dst` every `every_kb` KB read."""
+    nb = _nbytes(src) if nbytes is None else nbytes
+    _check(_lib.wq_probe_read_write(_ptr(src), nb, _ptr(dst), every_kb, _ptr(sink), _stream(stream)),
+           "wq_probe_read_write")
 
 
 def wq_probe_copy(src, dst, stream=None, nbytes: Optional[int] = None):

@@ -193,7 +193,12 @@ size_t wq_verify_workspace_bytes(const wq_matrix* descs, int count, int N);
  * requirements of its format's GEMM call; matrices may differ in format
  * and shape.  Results equal, bit for bit, those of the single-matrix
  * calls whenever wq_gemm_split reports the same split for both; otherwise
- * they agree to FP32 rounding of the sums. */
+ * they agree to FP32 rounding of the sums.  In a pass of tiled matrices
+ * only, a matrix split in K that is large next to a workgroup's share of
+ * the pass (32 or more of its 16-row tiles per workgroup) is computed in
+ * blocks of tiles whose chunk sums stay in the workgroup's LDS and are
+ * added in chunk order, as the separate reduction adds them: the same bits,
+ * no partial sums written, no reduction launch for it. */
 wq_status wq_verify_pass(const wq_matrix* descs, int count, int N,
                          void* workspace, size_t workspace_bytes, void* stream);
 
@@ -205,7 +210,9 @@ wq_status wq_verify_pass(const wq_matrix* descs, int count, int N,
  * kernel and can be called any number of times, on any stream ordered
  * after the copy, for as long as the workspace and every matrix buffer
  * stay alive and unchanged in place.  wq_verify_pass is prepare + launch.
- * The plan's fields are owned by the library; callers only keep it. */
+ * The plan's fields are owned by the library; callers only keep it
+ * (reduce_runs: reduction blocks launched after the pass, 0 when there are
+ * none; lds_extra: LDS bytes per workgroup for blocked chunk sums). */
 typedef struct wq_verify_plan {
   void* workspace;
   size_t workspace_bytes;
@@ -216,7 +223,7 @@ typedef struct wq_verify_plan {
   size_t ranges_offset;
   size_t reduce_offset;
   int32_t reduce_runs;
-  int32_t reserved;
+  int32_t lds_extra;
 } wq_verify_plan;
 
 wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N,
@@ -387,12 +394,26 @@ wq_status wq_mlp_chain_launch_persistent(const wq_mlp_plan* plan, void* stream);
  *  wq_probe_read: streams `bytes` (multiple of 16, src 16-byte aligned)
  *    with the 16-byte non-temporal loads the weight stream uses, writing one
  *    word per thread to `sink`, which must hold wq_probe_sink_words() words.
+ *    One workgroup of 8 waves per CU; each wave reads its own contiguous
+ *    share in whole 1 KB requests, 8 in flight.
+ *  wq_probe_read_write: the same read stream, plus, every `every_kb` KB a
+ *    wave reads (a multiple of 8), one 256-byte store of that wave to its own
+ *    consecutive slice of `dst`, written through to memory as the verify
+ *    pass writes its outputs: it prices output writes mixed into a weight
+ *    stream.  `dst` must hold wq_probe_read_write_bytes(bytes, every_kb)
+ *    bytes (16-byte aligned); a call writes at most that, and exactly that
+ *    when the waves' shares are of equal length (bytes a multiple of 16 x
+ *    the wave count, e.g. 4 GiB on 256 CUs).
  *  wq_probe_copy: copies `bytes` from src to dst (both 16-byte aligned,
  *    not overlapping): a kernel that reads and writes exactly `bytes`, for
  *    scaling hardware byte counters.
- * Both only enqueue on `stream`. */
+ * All only enqueue on `stream`; the read probes need a current device
+ * (WQ_ERROR_DEVICE otherwise) and return WQ_ERROR_UNSUPPORTED_SHAPE when a
+ * wave's share would reach 2 GiB. */
 size_t wq_probe_sink_words(void);
 wq_status wq_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+size_t wq_probe_read_write_bytes(size_t bytes, int every_kb);
+wq_status wq_probe_read_write(const void* src, size_t bytes, void* dst, int every_kb, uint32_t* sink, void* stream);
 wq_status wq_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus

@@ -284,3 +284,50 @@ def test_dynamic_tail_covers_every_unit_on_every_launch(wq):
         torch.cuda.synchronize()
         for m, (yr, ar) in zip(mats, refs):
             assert_close(m.y.cpu().numpy(), yr, ar, "launch %d M=%d" % (launch, m.M))
+
+
+def test_blocked_split_pass(wq):
+    # A pass large enough that its split matrix (K = 8736: two K chunks) is
+    # computed in blocks of tiles whose chunk sums stay in LDS, with no
+    # partial sums in the workspace and no reduction launch; the dynamic tail
+    # runs through it and on into a second matrix.  Every launch of three
+    # (outputs reset to NaN in between) must match the oracle on sampled rows,
+    # equal the single-matrix product (which adds the same chunk sums in a
+    # reduction kernel) bit for bit when the splits agree, and its first
+    # three columns must not depend on N.
+    specs = [(150000, 8736), (20000, 256)]
+    host = [inputs.nvfp4_inputs(M, K, 8, seed=1950 + i, g=0.02) for i, (M, K) in enumerate(specs)]
+    tiled = [to_tiled(wq, d) for d in host]
+    xs = [dev_bf16bits(d.x) for d in host]
+    outs = {}
+    for N in (3, 8):
+        mats = []
+        for d, t, x in zip(host, tiled, xs):
+            y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
+            mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, t, None, x[:N].contiguous(), y, d.g))
+        ws = workspace(wq.wq_verify_workspace_bytes(mats, N))
+        plan = wq.wq_verify_prepare(mats, N, ws)
+        print("blocked pass N=%d: reduce runs %d, lds_extra %d" % (N, plan.reduce_runs, plan.lds_extra), flush=True)
+        assert plan.reduce_runs == 0 and plan.lds_extra > 0
+        rng = np.random.default_rng(1960 + N)
+        refs = []
+        for d in host:
+            rows = np.unique(np.concatenate([rng.integers(0, d.M, 600), [0, d.M - 1]]))
+            refs.append((rows,) + oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N], rows=rows))
+        for launch in range(3):
+            for m in mats:
+                m.y.fill_(float("nan"))
+            print("blocked pass N=%d launch %d" % (N, launch), flush=True)
+            wq.wq_verify_launch(plan)
+            torch.cuda.synchronize()
+            for m, (rows, yr, ar) in zip(mats, refs):
+                assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "N=%d launch %d M=%d K=%d" % (N, launch, m.M, m.K))
+        outs[N] = [m.y.cpu().numpy() for m in mats]
+    for i, d in enumerate(host):
+        assert np.array_equal(outs[3][i].view(np.uint32), outs[8][i][:3].view(np.uint32)), "M=%d: N=3 differs" % d.M
+    d = host[0]
+    if wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K) == wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, True):
+        y1 = run_tiled(wq, d, 8)
+        assert np.array_equal(y1.view(np.uint32), outs[8][0].view(np.uint32))
+    else:
+        print("single-matrix split differs: bitwise comparison skipped", flush=True)
