@@ -59,6 +59,8 @@ struct Split {
   int nchunks = 0;
   int ntiles = 0;
   int tb = 0;  // tiles per block of a blocked split (all-tiled verify passes), else 0
+  uint32_t pa_off = 0;  // blocked: LDS byte of the first slot below the zero block
+  int pa_slots = 0;     // blocked: slots there
 };
 
 int seg_k(int fmt) {
@@ -81,6 +83,16 @@ Split make_split(int fmt, int M, int K, int kc) {
 Split verify_split(int fmt, int M, int K) {
   const int sk = seg_k(fmt);
   const int n = (int)ceil_div(K, kKcMax);
+  const int kc = (int)(ceil_div(ceil_div(K, n), sk) * sk);
+  return make_split(fmt, M, K, kc);
+}
+
+// A split matrix computed in blocks inside a verify pass: chunks of at most
+// kKcBlocked k, so that the space between its X chunk and the zero block
+// holds chunk-sum slots at every N (the chunking does not depend on N).
+Split blocked_split(int fmt, int M, int K) {
+  const int sk = seg_k(fmt);
+  const int n = (int)std::max(ceil_div(K, kKcMax), ceil_div(K, kKcBlocked));
   const int kc = (int)(ceil_div(ceil_div(K, n), sk) * sk);
   return make_split(fmt, M, K, kc);
 }
@@ -169,6 +181,8 @@ DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x
   d.ntiles = sp.ntiles;
   d.unit0 = unit0;
   d.tb = sp.tb;
+  d.pa_off = sp.pa_off;
+  d.pa_slots = sp.pa_slots;
   if (sp.nchunks > 1 && sp.tb == 0) d.part = reinterpret_cast<float*>(scratch);
   return d;
 }
@@ -265,8 +279,17 @@ PassLayout pass_layout(const wq_matrix* in, int count, int N, int cus) {
   const double share = total / L.grid;
   const bool tiled = all_tiled(in, count);
   std::vector<char> blk(count, 0);
-  for (int i = 0; i < count; ++i)
-    blk[i] = tiled && sp[i].nchunks > 1 && share >= kBlockMinTiles * tile_cost(in[i], sp[i]);
+  for (int i = 0; i < count; ++i) {
+    if (!tiled || sp[i].nchunks <= 1) continue;
+    const Split b = blocked_split(in[i].fmt, in[i].M, in[i].K);
+    if (share >= kBlockMinTiles * tile_cost(in[i], b)) {
+      blk[i] = 1;
+      // the same units, tile-major: the pass's total does not change
+      L.units += (int64_t)b.nchunks * b.ntiles - (int64_t)sp[i].nchunks * sp[i].ntiles;
+      sp[i] = b;
+    }
+  }
+  L.grid = (int)std::min<int64_t>(cus, L.units);
   int64_t blocked_tiles = 0;
   for (int pass = 0; pass < 2; ++pass)
     for (int i = 0; i < count; ++i) {
@@ -274,9 +297,14 @@ PassLayout pass_layout(const wq_matrix* in, int count, int N, int cus) {
       L.descs.push_back(in[i]);
       L.splits.push_back(sp[i]);
       if (blk[i]) {
-        L.splits.back().tb = part_tiles_for(N);
-        L.lds_extra = (uint32_t)part_tiles_for(N) * kPartTileBytes;
-        blocked_tiles += sp[i].ntiles;
+        Split& b = L.splits.back();
+        // slots between this matrix's X chunk (2 kc N bytes) and the zero
+        // block, then past the zero block
+        b.pa_off = 2u * (uint32_t)b.kc * (uint32_t)N;
+        b.pa_slots = (int)((2u * (uint32_t)(kKcMax - b.kc) * (uint32_t)N) / kPartTileBytes);
+        b.tb = std::min(kPartTilesMax, b.pa_slots + part_tiles_for(N));
+        L.lds_extra = std::max(L.lds_extra, (uint32_t)std::max(0, b.tb - b.pa_slots) * kPartTileBytes);
+        blocked_tiles += b.ntiles;
       }
     }
   L.scratch_off.resize(count);
@@ -539,7 +567,9 @@ wq_status wq_gemm_split(int fmt, int M, int K, int in_verify_pass, int* k_chunk,
   wq_status st = check_shape(fmt, M, K, 1);
   if (st != WQ_SUCCESS) return st;
   Split sp;
-  if (in_verify_pass) {
+  if (in_verify_pass == 2) {
+    sp = is_tiled(fmt) ? blocked_split(fmt, M, K) : verify_split(fmt, M, K);
+  } else if (in_verify_pass) {
     sp = verify_split(fmt, M, K);
   } else {
     const int cus = current_cus();

@@ -58,16 +58,16 @@ constexpr uint32_t kArgLdsBytes = 512;
 constexpr uint32_t kLdsLimit = 160u * 1024u - 256u;
 // A large split matrix of an all-tiled verify pass is processed in blocks of
 // tiles: one workgroup computes every K chunk of a block in turn and keeps
-// the block's chunk sums in LDS past the zero block (32 lanes x 4 floats per
-// tile), so no partial sums leave the CU and no reduction launch follows.
-// A block holds as many tiles as the LDS left at N allows (40 at N = 8).
+// the block's chunk sums in LDS (32 lanes x 4 floats per tile), so no
+// partial sums leave the CU and no reduction launch follows.  Its K chunks
+// are at most kKcBlocked long, which leaves LDS free between its X chunk and
+// the zero block; a block holds as many tiles as that space and the LDS past
+// the zero block allow (127 at N = 8).
+constexpr int kKcBlocked = 6144;
 constexpr uint32_t kPartTileBytes = 512;
 constexpr int kPartTilesMax = 256;
-constexpr int part_tiles_for(int n) {
-  return (int)((kLdsLimit - lds_bytes_for(n)) / kPartTileBytes) < kPartTilesMax
-             ? (int)((kLdsLimit - lds_bytes_for(n)) / kPartTileBytes)
-             : kPartTilesMax;
-}
+// slots past the zero block at n columns
+constexpr int part_tiles_for(int n) { return (int)((kLdsLimit - lds_bytes_for(n)) / kPartTileBytes); }
 template <int N>
 __host__ __device__ constexpr uint32_t kPartOffset() { return kZeroOffset<N>() + kZeroBytes<N>(); }
 constexpr uint32_t kMaxLdsBytes = kLdsLimit;
@@ -112,7 +112,12 @@ struct DevMat {
   // per block, else 0.  The matrix's units are then tile-major (unit =
   // tile * nchunks + chunk), a workgroup's range holds whole tiles, and the
   // workgroup takes them tb at a time, every chunk of such a block in turn.
+  // A block's 512-byte slots: the first pa_slots at LDS byte pa_off (past
+  // this matrix's own X chunk, below the zero block), the rest past the
+  // zero block (kPartOffset).
   int tb;
+  uint32_t pa_off;
+  int pa_slots;
 };
 
 // First unit (and the matrix holding it) of each workgroup's run.

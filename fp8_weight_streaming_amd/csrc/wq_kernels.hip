@@ -486,9 +486,9 @@ constexpr int kEpiGlu = 2;
 // Units [first, end) are tiles first - ubase .. end - 1 - ubase of chunk
 // `chunk`.  ptile0 >= 0 marks a blocked split matrix (DevMat::tb) whose
 // block starts at tile ptile0 (BLK kernels only): the chunk sums of the
-// block's tiles wait in LDS (one 512-byte slot per tile of the block) for
-// the next chunk, which adds its own to them, in chunk order as
-// reduce_kernel does, and the last chunk stores y.
+// block's tiles wait in LDS (one 512-byte slot per tile of the block, placed
+// as DevMat::pa_off / pa_slots say) for the next chunk, which adds its own
+// to them, in chunk order as reduce_kernel does, and the last chunk stores y.
 template <int N, int PF, bool FP8, int EPI, bool BLK, typename Pre, typename Stage>
 __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, int64_t ubase, int ptile0,
                           char* lds, uint64_t* bestk, Pre&& pre, Stage&& stage) {
@@ -651,7 +651,10 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       // blocked: lane l and l + 32 hold the same (n, m), so both read the
       // slot of lane l % 32; lanes 0..31 write it
       f32x4 pin = {0.f, 0.f, 0.f, 0.f}, pout;
-      const uint32_t poff = kPartOffset<N>() + (uint32_t)(((tile0 + ci - ptile0) * 32 + (lane & 31)) * 16);
+      const int pslot = tile0 + ci - ptile0;
+      const uint32_t poff = (pslot < mt.pa_slots ? mt.pa_off + (uint32_t)pslot * kPartTileBytes
+                                                 : kPartOffset<N>() + (uint32_t)(pslot - mt.pa_slots) * kPartTileBytes) +
+                            (uint32_t)(lane & 31) * 16u;
       if (from_lds) pin = *reinterpret_cast<const f32x4*>(lds + poff);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

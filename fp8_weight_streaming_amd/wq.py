@@ -199,10 +199,11 @@ def wq_gemm_workspace_bytes(fmt: int, M: int, K: int, N: int) -> int:
     return int(_lib.wq_gemm_workspace_bytes(fmt, M, K, N))
 
 
-def wq_gemm_split(fmt: int, M: int, K: int, in_verify_pass: bool = False):
-    """(k_chunk, n_chunks) the call would use."""
+def wq_gemm_split(fmt: int, M: int, K: int, in_verify_pass: int = 0):
+    """(k_chunk, n_chunks) the call would use (in_verify_pass: 0 single call, 1 or True in a verify pass,
+    2 computed in blocks in a verify pass)."""
     kc, nc = _I(0), _I(0)
-    _check(_lib.wq_gemm_split(fmt, M, K, 1 if in_verify_pass else 0, ctypes.byref(kc), ctypes.byref(nc)),
+    _check(_lib.wq_gemm_split(fmt, M, K, int(in_verify_pass), ctypes.byref(kc), ctypes.byref(nc)),
            "wq_gemm_split")
     return kc.value, nc.value
 

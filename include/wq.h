@@ -75,7 +75,9 @@ size_t wq_gemm_workspace_bytes(int fmt, int M, int K, int N);
 /* The K split a call will use: K is cut into *n_chunks chunks of *k_chunk
  * (the last may be shorter).  in_verify_pass = 0 asks about
  * wq_gemm_nvfp4 / wq_gemm_fp8row on the current device, 1 about a matrix
- * inside wq_verify_pass.  Two calls that report the same split compute
+ * inside wq_verify_pass, 2 about a matrix that wq_verify_pass computes in
+ * blocks (a large split matrix of a pass of tiled matrices only; see
+ * wq_verify_pass).  Two calls that report the same split compute
  * bit-identical results for the same matrix and columns. */
 wq_status wq_gemm_split(int fmt, int M, int K, int in_verify_pass, int* k_chunk, int* n_chunks);
 

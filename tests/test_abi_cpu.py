@@ -106,6 +106,14 @@ def test_split_query_rejects_bad_args(wq):
     assert (kc.value, nc.value) == (5120, 1)
     assert lib.wq_gemm_split(1, 151936, 5120, 1, ctypes.byref(kc), ctypes.byref(nc)) == 0
     assert (kc.value, nc.value) == (5120, 1)
+    # computed in blocks inside a verify pass (tiled formats): chunks of at
+    # most 6144 k, whole 256-k steps, as even as that allows
+    assert lib.wq_gemm_split(2, 5120, 17408, 2, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (5888, 3)
+    assert lib.wq_gemm_split(2, 150000, 8736, 2, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (4608, 2)
+    assert lib.wq_gemm_split(3, 64, 17424, 2, ctypes.byref(kc), ctypes.byref(nc)) == 0
+    assert (kc.value, nc.value) == (5888, 3)
 
 
 def fp8t(lib, w=FAKE, rs=FAKE, x=FAKE, y=FAKE, M=64, K=128, N=4, ws=0, wsb=0):

@@ -326,7 +326,7 @@ def test_blocked_split_pass(wq):
     for i, d in enumerate(host):
         assert np.array_equal(outs[3][i].view(np.uint32), outs[8][i][:3].view(np.uint32)), "M=%d: N=3 differs" % d.M
     d = host[0]
-    if wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K) == wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, True):
+    if wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K) == wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, 2):
         y1 = run_tiled(wq, d, 8)
         assert np.array_equal(y1.view(np.uint32), outs[8][0].view(np.uint32))
     else:
