@@ -58,9 +58,7 @@ struct Split {
   int kc = 0;
   int nchunks = 0;
   int ntiles = 0;
-  int tb = 0;  // tiles per block of a blocked split (all-tiled verify passes), else 0
-  uint32_t pa_off = 0;  // blocked: LDS byte of the first slot below the zero block
-  int pa_slots = 0;     // blocked: slots there
+  int tb = 0;  // 1 for a blocked split (all-tiled verify passes), else 0
 };
 
 int seg_k(int fmt) {
@@ -181,8 +179,6 @@ DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x
   d.ntiles = sp.ntiles;
   d.unit0 = unit0;
   d.tb = sp.tb;
-  d.pa_off = sp.pa_off;
-  d.pa_slots = sp.pa_slots;
   if (sp.nchunks > 1 && sp.tb == 0) d.part = reinterpret_cast<float*>(scratch);
   return d;
 }
@@ -297,14 +293,11 @@ PassLayout pass_layout(const wq_matrix* in, int count, int N, int cus) {
       L.descs.push_back(in[i]);
       L.splits.push_back(sp[i]);
       if (blk[i]) {
-        Split& b = L.splits.back();
-        // slots between this matrix's X chunk (2 kc N bytes) and the zero
-        // block, then past the zero block
-        b.pa_off = 2u * (uint32_t)b.kc * (uint32_t)N;
-        b.pa_slots = (int)((2u * (uint32_t)(kKcMax - b.kc) * (uint32_t)N) / kPartTileBytes);
-        b.tb = std::min(kPartTilesMax, b.pa_slots + part_tiles_for(N));
-        L.lds_extra = std::max(L.lds_extra, (uint32_t)std::max(0, b.tb - b.pa_slots) * kPartTileBytes);
-        blocked_tiles += b.ntiles;
+        // the kernel places the block's slots (part_a_slots, block_tiles) in
+        // all the LDS a workgroup may have
+        L.splits.back().tb = 1;
+        L.lds_extra = kLdsLimit - lds_bytes_for(N);
+        blocked_tiles += sp[i].ntiles;
       }
     }
   L.scratch_off.resize(count);
@@ -316,8 +309,8 @@ PassLayout pass_layout(const wq_matrix* in, int count, int N, int cus) {
   }
   L.table_bytes = align_up((size_t)count * sizeof(DevMat), kAlign);
   // claims: at most one per kDynChunkMin units, or per tile of a blocked
-  // matrix, plus one per matrix (a claim may end at a matrix's end), plus
-  // the end entry
+  // matrix, plus one per matrix (a claim may end at a blocked matrix's end),
+  // plus the end entry
   L.dyn_chunks = ceil_div(L.units, kDynChunkMin) + blocked_tiles + count + 1;
   L.ranges_bytes = align_up((size_t)(L.grid + 1) * sizeof(WgRange) + sizeof(DynSched) +
                                 (size_t)L.dyn_chunks * sizeof(DynClaim),
@@ -399,10 +392,10 @@ std::vector<WgRange> balance(const wq_matrix* descs, int count, const PassLayout
 }
 
 // The dynamic tail [dyn_begin, units) as claims, each followed by the next
-// one's begin (the last entry only ends the tail): `chunk` units, rounded up
-// to whole tiles where a claim ends inside a blocked matrix (whose units are
-// tile-major); a claim starting in a blocked matrix takes chunk / nchunks
-// tiles of it (at least one).
+// one's begin (the last entry only ends the tail): `chunk` units; a claim
+// starting in a blocked matrix (tile-major units) takes chunk / nchunks
+// whole tiles of it (at least one).  Blocked matrices lead the unit list,
+// so a claim starting elsewhere never reaches one.
 std::vector<DynClaim> tail_claims(const std::vector<DevMat>& mats, const PassLayout& L, int64_t dyn_begin,
                                   int chunk) {
   const int count = (int)mats.size();
@@ -421,9 +414,6 @@ std::vector<DynClaim> tail_claims(const std::vector<DevMat>& mats, const PassLay
       e = tile_end(i, u + tiles * L.splits[i].nchunks);
     } else {
       e = std::min<int64_t>(u + chunk, L.units);
-      int j = i;  // the matrix holding unit e - 1
-      while (j + 1 < count && mats[j + 1].unit0 < e) ++j;
-      if (L.splits[j].tb > 0) e = tile_end(j, e);
     }
     claims.push_back(DynClaim{u, i, 0});
     u = e;
@@ -718,9 +708,7 @@ wq_status wq_verify_prepare(const wq_matrix* descs, int count, int N, void* work
 // LDS past the X chunk and the zero block: the blocked chunk sums of an
 // all-tiled pass, or nothing
 static bool lds_extra_ok(const wq_verify_plan& p) {
-  return p.lds_extra == 0 ||
-         (p.mode == kModeTiled && p.lds_extra > 0 && p.lds_extra % kPartTileBytes == 0 &&
-          lds_bytes_for(p.N) + (uint32_t)p.lds_extra <= kLdsLimit);
+  return p.lds_extra == 0 || (p.mode == kModeTiled && lds_bytes_for(p.N) + (uint32_t)p.lds_extra == kLdsLimit);
 }
 
 wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {

@@ -49,7 +49,7 @@ __host__ __device__ constexpr uint32_t kZeroOffset() { return (uint32_t)kKcMax *
 // tiled NVFP4 reads at up to 256N (second half) + 3*64N (MFMA step) + 16.
 template <int N>
 __host__ __device__ constexpr uint32_t kZeroBytes() { return 512u * N; }
-constexpr uint32_t lds_bytes_for(int n) { return (uint32_t)kKcMax * 2u * n + 512u * n; }
+__host__ __device__ constexpr uint32_t lds_bytes_for(int n) { return (uint32_t)kKcMax * 2u * n + 512u * n; }
 // Head acceptance (kModeTiledArgmax) adds, past the zero block, each wave's
 // best keys: 8 waves x 8 columns x 8 bytes.
 constexpr uint32_t kArgLdsBytes = 512;
@@ -67,9 +67,23 @@ constexpr int kKcBlocked = 6144;
 constexpr uint32_t kPartTileBytes = 512;
 constexpr int kPartTilesMax = 256;
 // slots past the zero block at n columns
-constexpr int part_tiles_for(int n) { return (int)((kLdsLimit - lds_bytes_for(n)) / kPartTileBytes); }
+__host__ __device__ constexpr int part_tiles_for(int n) {
+  return (int)((kLdsLimit - lds_bytes_for(n)) / kPartTileBytes);
+}
 template <int N>
 __host__ __device__ constexpr uint32_t kPartOffset() { return kZeroOffset<N>() + kZeroBytes<N>(); }
+// A block's 512-byte slots at N columns for a blocked matrix with K chunks of
+// kc: the first part_a_slots at LDS byte 2 kc N (past its own X chunk, below
+// the zero block), the rest past the zero block, within kLdsLimit.
+template <int N>
+__host__ __device__ constexpr int part_a_slots(int kc) {
+  return (int)((2u * (uint32_t)(kKcMax - kc) * (uint32_t)N) / kPartTileBytes);
+}
+template <int N>
+__host__ __device__ constexpr int block_tiles(int kc) {
+  return part_a_slots<N>(kc) + part_tiles_for(N) < kPartTilesMax ? part_a_slots<N>(kc) + part_tiles_for(N)
+                                                                  : kPartTilesMax;
+}
 constexpr uint32_t kMaxLdsBytes = kLdsLimit;
 static_assert(lds_bytes_for(8) + kArgLdsBytes <= kLdsLimit, "LDS budget exceeded");
 static_assert(part_tiles_for(8) >= 32, "too few tiles per block at N = 8");
@@ -108,16 +122,13 @@ struct DevMat {
   float g2;
   float eps;
   int nparts;
-  // Blocked split (large split matrices of all-tiled verify passes): tiles
-  // per block, else 0.  The matrix's units are then tile-major (unit =
-  // tile * nchunks + chunk), a workgroup's range holds whole tiles, and the
-  // workgroup takes them tb at a time, every chunk of such a block in turn.
-  // A block's 512-byte slots: the first pa_slots at LDS byte pa_off (past
-  // this matrix's own X chunk, below the zero block), the rest past the
-  // zero block (kPartOffset).
+  // Blocked split (large split matrices of all-tiled verify passes): 1,
+  // else 0.  The matrix's units are then tile-major (unit = tile * nchunks +
+  // chunk), a workgroup's range holds whole tiles, and the workgroup takes
+  // them block_tiles<N>(kc) at a time, every chunk of such a block in turn
+  // (a launch of a blocked plan has kLdsLimit bytes of dynamic LDS).
   int tb;
-  uint32_t pa_off;
-  int pa_slots;
+  int pad2;
 };
 
 // First unit (and the matrix holding it) of each workgroup's run.

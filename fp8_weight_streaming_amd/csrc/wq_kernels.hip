@@ -487,8 +487,8 @@ constexpr int kEpiGlu = 2;
 // `chunk`.  ptile0 >= 0 marks a blocked split matrix (DevMat::tb) whose
 // block starts at tile ptile0 (BLK kernels only): the chunk sums of the
 // block's tiles wait in LDS (one 512-byte slot per tile of the block, placed
-// as DevMat::pa_off / pa_slots say) for the next chunk, which adds its own
-// to them, in chunk order as reduce_kernel does, and the last chunk stores y.
+// as part_a_slots says) for the next chunk, which adds its own to them, in
+// chunk order as reduce_kernel does, and the last chunk stores y.
 template <int N, int PF, bool FP8, int EPI, bool BLK, typename Pre, typename Stage>
 __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, int64_t ubase, int ptile0,
                           char* lds, uint64_t* bestk, Pre&& pre, Stage&& stage) {
@@ -652,8 +652,9 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       // slot of lane l % 32; lanes 0..31 write it
       f32x4 pin = {0.f, 0.f, 0.f, 0.f}, pout;
       const int pslot = tile0 + ci - ptile0;
-      const uint32_t poff = (pslot < mt.pa_slots ? mt.pa_off + (uint32_t)pslot * kPartTileBytes
-                                                 : kPartOffset<N>() + (uint32_t)(pslot - mt.pa_slots) * kPartTileBytes) +
+      const int na = part_a_slots<N>(mt.kc);
+      const uint32_t poff = (pslot < na ? 2u * (uint32_t)mt.kc * N + (uint32_t)pslot * kPartTileBytes
+                                        : kPartOffset<N>() + (uint32_t)(pslot - na) * kPartTileBytes) +
                             (uint32_t)(lane & 31) * 16u;
       if (from_lds) pin = *reinterpret_cast<const f32x4*>(lds + poff);
 #pragma unroll
@@ -916,15 +917,15 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     const int64_t local = u - mt.unit0;
     // The segment: units [first, run_end) of one K chunk, tile = unit - ubase.
     // A blocked split's units are tile-major (tile * nchunks + chunk) and a
-    // range holds whole tiles: the run takes them mt.tb at a time, all chunks
-    // of such a block in turn (bchunk counts them), and moves u past the
-    // block after its last chunk.
+    // range holds whole tiles: the run takes them block_tiles at a time, all
+    // chunks of such a block in turn (bchunk counts them), and moves u past
+    // the block after its last chunk.
     int chunk, ptile0 = -1;
     int64_t first, run_end, ubase;
     if (mt.tb > 0) {
       const int nc = mt.nchunks;
       const int t0 = (int)(local / nc);
-      const int t1 = min(t0 + mt.tb, (int)((min(u_end, mend) - mt.unit0) / nc));
+      const int t1 = min(t0 + block_tiles<N>(mt.kc), (int)((min(u_end, mend) - mt.unit0) / nc));
       chunk = bchunk;
       first = t0;
       run_end = t1;
