@@ -164,8 +164,10 @@ struct DynClaim {
 // units per workgroup / 32, within [8, 16] (16 for the dense 64-layer
 // pass).  A chunk's fixed cost (X restaging, the ring's ramp) wants it
 // large, the balance at the end wants it small next to a workgroup's work;
-// passes under kDynMinUnitsPerWg units per workgroup have no tail.
-constexpr double kDynShare = 0.08;
+// passes under kDynMinUnitsPerWg units per workgroup have no tail.  (Dense
+// 64-layer pass, one box, N = 2 / 4 / 8: a 3% share 1800 / 1858 / 1977 us,
+// 5% 1775 / 1839 / 1961, 6% 1776 / 1837 / 1960, 8% 1800 / 1843 / 1973.)
+constexpr double kDynShare = 0.05;
 constexpr int kDynChunkMin = 8;
 constexpr int kDynChunkMax = 16;
 constexpr int kDynMinUnitsPerWg = 256;
