@@ -831,6 +831,7 @@ def main():
                 "kernel": "wq::stream_kernel<N, tiled-NVFP4 mode> + wq::reduce_kernel (one verify pass)",
                 "avg_launch_us": kernel_s / steps * 1e6,
                 "algorithmic_bytes_per_launch_mean": total_bytes / steps,
+                "traffic_gbps": (traffic / (kernel_s / steps) / 1e9) if traffic else None,
                 "probe_read_gbps": probe_gbps, "frac_of_probe": achieved / probe_gbps,
                 "probe_write_cost": write_probe}
 

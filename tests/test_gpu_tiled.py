@@ -287,33 +287,43 @@ def test_dynamic_tail_covers_every_unit_on_every_launch(wq):
 
 
 def test_blocked_split_pass(wq):
-    # A pass large enough that its split matrix (K = 8736: two K chunks) is
+    # A pass large enough that its split matrices (tiled NVFP4, K = 8736, and
+    # tiled FP8-row, K = 8720: two K chunks each, ragged last tiles) are
     # computed in blocks of tiles whose chunk sums stay in LDS, with no
-    # partial sums in the workspace and no reduction launch; the dynamic tail
-    # runs through it and on into a second matrix.  Every launch of three
+    # partial sums in the workspace and no reduction launch, ahead of a third
+    # matrix that holds the dynamic tail (the planner's host test covers tail
+    # claims inside blocked matrices).  Every launch of three
     # (outputs reset to NaN in between) must match the oracle on sampled rows,
-    # equal the single-matrix product (which adds the same chunk sums in a
-    # reduction kernel) bit for bit when the splits agree, and its first
+    # equal the single-matrix products (which add the same chunk sums in a
+    # reduction kernel) bit for bit when the splits agree, and the first
     # three columns must not depend on N.
-    specs = [(150000, 8736), (20000, 256)]
-    host = [inputs.nvfp4_inputs(M, K, 8, seed=1950 + i, g=0.02) for i, (M, K) in enumerate(specs)]
-    tiled = [to_tiled(wq, d) for d in host]
-    xs = [dev_bf16bits(d.x) for d in host]
+    host = [("nvfp4", inputs.nvfp4_inputs(150007, 8736, 8, seed=1950, g=0.02)),
+            ("fp8", inputs.fp8row_inputs(60011, 8720, 8, seed=1951)),
+            ("nvfp4", inputs.nvfp4_inputs(700000, 256, 8, seed=1952, g=0.02))]
+    tiled = [to_tiled(wq, d) if f == "nvfp4" else to_fp8_tiled(wq, d) for f, d in host]
+    xs = [dev_bf16bits(d.x) for _, d in host]
+    rss = [dev_f32(d.row_scale) if f == "fp8" else None for f, d in host]
     outs = {}
     for N in (3, 8):
         mats = []
-        for d, t, x in zip(host, tiled, xs):
+        for (f, d), t, x, rs in zip(host, tiled, xs, rss):
             y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
-            mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, t, None, x[:N].contiguous(), y, d.g))
+            if f == "nvfp4":
+                mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, t, None, x[:N].contiguous(), y, d.g))
+            else:
+                mats.append(wq.Matrix(wq.WQ_FMT_FP8ROW_TILED, d.M, d.K, t, rs, x[:N].contiguous(), y, 1.0))
         ws = workspace(wq.wq_verify_workspace_bytes(mats, N))
         plan = wq.wq_verify_prepare(mats, N, ws)
         print("blocked pass N=%d: reduce runs %d, lds_extra %d" % (N, plan.reduce_runs, plan.lds_extra), flush=True)
         assert plan.reduce_runs == 0 and plan.lds_extra > 0
         rng = np.random.default_rng(1960 + N)
         refs = []
-        for d in host:
-            rows = np.unique(np.concatenate([rng.integers(0, d.M, 600), [0, d.M - 1]]))
-            refs.append((rows,) + oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N], rows=rows))
+        for f, d in host:
+            rows = np.unique(np.concatenate([rng.integers(0, d.M, 600), np.arange(d.M - 16, d.M), [0]]))
+            if f == "nvfp4":
+                refs.append((rows,) + oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N], rows=rows))
+            else:
+                refs.append((rows,) + oracle.gemm_fp8row(d.w, d.row_scale, d.x[:N], rows=rows))
         for launch in range(3):
             for m in mats:
                 m.y.fill_(float("nan"))
@@ -323,11 +333,12 @@ def test_blocked_split_pass(wq):
             for m, (rows, yr, ar) in zip(mats, refs):
                 assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "N=%d launch %d M=%d K=%d" % (N, launch, m.M, m.K))
         outs[N] = [m.y.cpu().numpy() for m in mats]
-    for i, d in enumerate(host):
+    for i, (_, d) in enumerate(host):
         assert np.array_equal(outs[3][i].view(np.uint32), outs[8][i][:3].view(np.uint32)), "M=%d: N=3 differs" % d.M
-    d = host[0]
-    if wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K) == wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, 2):
-        y1 = run_tiled(wq, d, 8)
-        assert np.array_equal(y1.view(np.uint32), outs[8][0].view(np.uint32))
-    else:
-        print("single-matrix split differs: bitwise comparison skipped", flush=True)
+    for i, (f, d) in enumerate(host[:2]):
+        fmt = wq.WQ_FMT_NVFP4_TILED if f == "nvfp4" else wq.WQ_FMT_FP8ROW_TILED
+        if wq.wq_gemm_split(fmt, d.M, d.K) == wq.wq_gemm_split(fmt, d.M, d.K, 2):
+            y1 = run_tiled(wq, d, 8) if f == "nvfp4" else run_fp8_tiled(wq, d, 8)
+            assert np.array_equal(y1.view(np.uint32), outs[8][i].view(np.uint32)), "%s M=%d" % (f, d.M)
+        else:
+            print("%s: single-matrix split differs: bitwise comparison skipped" % f, flush=True)
