@@ -280,7 +280,7 @@ PassLayout pass_layout(const wq_matrix* in, int count, int N, int cus) {
     const Split b = blocked_split(in[i].fmt, in[i].M, in[i].K);
     if (share >= kBlockMinTiles * tile_cost(in[i], b)) {
       blk[i] = 1;
-      // the same units, tile-major: the pass's total does not change
+      // its units follow its own (finer) chunking
       L.units += (int64_t)b.nchunks * b.ntiles - (int64_t)sp[i].nchunks * sp[i].ntiles;
       sp[i] = b;
     }
