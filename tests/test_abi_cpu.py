@@ -196,6 +196,22 @@ def test_device_n_launch_argument_errors(wq):
     assert lib.wq_verify_launch_n(C.byref(plan), FAKE, 0) == 1         # not an all-tiled plan
 
 
+def test_verify_launch_rejects_bad_lds_extra(wq):
+    # a blocked plan's workgroups have all the LDS: lds_extra is either 0 or
+    # exactly what brings the launch to the limit, and only for the tiled kernel
+    import ctypes as C
+    lib = wq.lib()
+    plan = wq.WqVerifyPlan()
+    plan.workspace, plan.workspace_bytes, plan.count, plan.N, plan.mode, plan.grid = FAKE, 1 << 20, 2, 8, 4, 1
+    plan.ranges_offset = 256
+    for extra in (512, 123, -512, 1 << 20):
+        plan.lds_extra = extra
+        assert lib.wq_verify_launch(C.byref(plan), 0) == 1
+        assert lib.wq_verify_launch_n(C.byref(plan), FAKE, 0) == 1
+    plan.mode, plan.N, plan.lds_extra = 0, 2, 512
+    assert lib.wq_verify_launch(C.byref(plan), 0) == 1                 # blocked LDS on a plain-layout plan
+
+
 def test_chain_argument_errors(wq):
     import ctypes as C
     lib = wq.lib()
