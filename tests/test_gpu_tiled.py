@@ -295,8 +295,8 @@ def test_blocked_split_pass(wq):
     # claims inside blocked matrices).  Every launch of three
     # (outputs reset to NaN in between) must match the oracle on sampled rows,
     # equal the single-matrix products (which add the same chunk sums in a
-    # reduction kernel) bit for bit when the splits agree, and the first
-    # three columns must not depend on N.
+    # reduction kernel) bit for bit when the splits agree, and column n must
+    # not depend on N (N = 1, 3, 5 against 8: different block sizes).
     host = [("nvfp4", inputs.nvfp4_inputs(150007, 8736, 8, seed=1950, g=0.02)),
             ("fp8", inputs.fp8row_inputs(60011, 8720, 8, seed=1951)),
             ("nvfp4", inputs.nvfp4_inputs(700000, 256, 8, seed=1952, g=0.02))]
@@ -304,7 +304,7 @@ def test_blocked_split_pass(wq):
     xs = [dev_bf16bits(d.x) for _, d in host]
     rss = [dev_f32(d.row_scale) if f == "fp8" else None for f, d in host]
     outs = {}
-    for N in (3, 8):
+    for N in (1, 3, 5, 8):
         mats = []
         for (f, d), t, x, rs in zip(host, tiled, xs, rss):
             y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
@@ -334,7 +334,8 @@ def test_blocked_split_pass(wq):
                 assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "N=%d launch %d M=%d K=%d" % (N, launch, m.M, m.K))
         outs[N] = [m.y.cpu().numpy() for m in mats]
     for i, (_, d) in enumerate(host):
-        assert np.array_equal(outs[3][i].view(np.uint32), outs[8][i][:3].view(np.uint32)), "M=%d: N=3 differs" % d.M
+        for N in (1, 3, 5):
+            assert np.array_equal(outs[N][i].view(np.uint32), outs[8][i][:N].view(np.uint32)), "M=%d: N=%d differs" % (d.M, N)
     for i, (f, d) in enumerate(host[:2]):
         fmt = wq.WQ_FMT_NVFP4_TILED if f == "nvfp4" else wq.WQ_FMT_FP8ROW_TILED
         if wq.wq_gemm_split(fmt, d.M, d.K) == wq.wq_gemm_split(fmt, d.M, d.K, 2):
