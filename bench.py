@@ -546,27 +546,32 @@ def draft_step_row(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows
     return row
 
 
-def device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n, reps=9):
+def device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n, reps=10, warm=3):
     """The pass launched with its column count in device memory
-    (wq_verify_launch_n on one plan prepared for N = 8), per N."""
+    (wq_verify_launch_n on one plan prepared for N = 8), timed as the main
+    loop is: N cycled 2, 4, 8 launch after launch (the count written to
+    device memory before each, outside the events), `warm` untimed cycles
+    first, then `reps` timed cycles; the mean per N."""
     dev = torch.device("cuda:0")
     mats = [wq.Matrix(wq.WQ_FMT_NVFP4_TILED, s.M, s.K, t, None, x, y, wl.g)
             for s, (c, sc, x, y, t) in zip(wl.matrices, mats_dev)]
     ws = torch.zeros(wq.wq_verify_workspace_bytes(mats, 8), dtype=torch.uint8, device=dev)
     plan = wq.wq_verify_prepare(mats, 8, ws, stream)
     n_dev = torch.zeros(1, dtype=torch.int32, device=dev)
-    out = {}
-    for N in N_CYCLE:
-        n_dev.fill_(N)
-        for _ in range(4):
-            wq.wq_verify_launch_n(plan, n_dev, stream)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in ev:
+    times = {N: [] for N in N_CYCLE}
+    for cycle in range(warm + reps):
+        for N in N_CYCLE:
+            n_dev.fill_(N)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             wq.wq_verify_launch_n(plan, n_dev, stream)
             b.record(stream)
-        torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+            if cycle >= warm:
+                times[N].append((a, b))
+    torch.cuda.synchronize()
+    out = {}
+    for N in N_CYCLE:
+        us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in times[N]]))
         out[str(N)] = {"us_per_pass_mean": us, "gbps": bytes_n[N] / us / 1e3,
                        "pct_of_8TBps": 100 * bytes_n[N] / us / 1e3 / PEAK_GBPS}
     return out
