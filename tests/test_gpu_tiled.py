@@ -343,3 +343,68 @@ def test_blocked_split_pass(wq):
             assert np.array_equal(y1.view(np.uint32), outs[8][i].view(np.uint32)), "%s M=%d" % (f, d.M)
         else:
             print("%s: single-matrix split differs: bitwise comparison skipped" % f, flush=True)
+
+
+def test_blocked_split_three_chunks_dense_down_shape(wq):
+    # The dense pass's own down-projection split: K = 17408 (tiled NVFP4) and
+    # K = 17424 (tiled FP8-row) computed in blocks of three K chunks of 5888
+    # (the last FP8 chunk ragged, 5648).  The middle chunk is the only one
+    # that both adds to a tile's running sums kept in LDS and leaves them
+    # there for the next chunk.  A third matrix holds the dynamic tail.  Four
+    # N (1, 2, 4, 8), three launches each with the outputs reset to NaN in
+    # between: sampled rows (the last 16 of each matrix included) against the
+    # oracle, column n the same bits for every N, and the single-matrix
+    # products bit for bit wherever they use the same split.
+    host = [("nvfp4", inputs.nvfp4_inputs(200003, 17408, 8, seed=1970, g=0.02)),
+            ("fp8", inputs.fp8row_inputs(40009, 17424, 8, seed=1971)),
+            ("nvfp4", inputs.nvfp4_inputs(700000, 256, 8, seed=1972, g=0.02))]
+    for f, d in host[:2]:
+        fmt = wq.WQ_FMT_NVFP4_TILED if f == "nvfp4" else wq.WQ_FMT_FP8ROW_TILED
+        assert wq.wq_gemm_split(fmt, d.M, d.K, 2) == (5888, 3), (f, wq.wq_gemm_split(fmt, d.M, d.K, 2))
+    tiled = [to_tiled(wq, d) if f == "nvfp4" else to_fp8_tiled(wq, d) for f, d in host]
+    xs = [dev_bf16bits(d.x) for _, d in host]
+    rss = [dev_f32(d.row_scale) if f == "fp8" else None for f, d in host]
+    outs = {}
+    for N in (1, 2, 4, 8):
+        mats = []
+        for (f, d), t, x, rs in zip(host, tiled, xs, rss):
+            y = torch.full((N, d.M), float("nan"), dtype=torch.float32, device=DEV)
+            if f == "nvfp4":
+                mats.append(wq.Matrix(wq.WQ_FMT_NVFP4_TILED, d.M, d.K, t, None, x[:N].contiguous(), y, d.g))
+            else:
+                mats.append(wq.Matrix(wq.WQ_FMT_FP8ROW_TILED, d.M, d.K, t, rs, x[:N].contiguous(), y, 1.0))
+        ws = workspace(wq.wq_verify_workspace_bytes(mats, N))
+        plan = wq.wq_verify_prepare(mats, N, ws)
+        print("3-chunk blocked pass N=%d: reduce runs %d, lds_extra %d" % (N, plan.reduce_runs, plan.lds_extra),
+              flush=True)
+        assert plan.reduce_runs == 0 and plan.lds_extra > 0
+        rng = np.random.default_rng(1980 + N)
+        refs = []
+        for f, d in host:
+            rows = np.unique(np.concatenate([rng.integers(0, d.M, 600), np.arange(d.M - 16, d.M), [0]]))
+            if f == "nvfp4":
+                refs.append((rows,) + oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N], rows=rows))
+            else:
+                refs.append((rows,) + oracle.gemm_fp8row(d.w, d.row_scale, d.x[:N], rows=rows))
+        for launch in range(3):
+            for m in mats:
+                m.y.fill_(float("nan"))
+            print("3-chunk blocked pass N=%d launch %d" % (N, launch), flush=True)
+            wq.wq_verify_launch(plan)
+            torch.cuda.synchronize()
+            for m, (rows, yr, ar) in zip(mats, refs):
+                assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "N=%d launch %d M=%d K=%d" % (N, launch, m.M, m.K))
+        outs[N] = [m.y.cpu().numpy() for m in mats]
+        del mats, ws, plan
+    for i, (_, d) in enumerate(host):
+        for N in (1, 2, 4):
+            assert np.array_equal(outs[N][i].view(np.uint32), outs[8][i][:N].view(np.uint32)), \
+                "M=%d K=%d: N=%d differs from N=8" % (d.M, d.K, N)
+    for i, (f, d) in enumerate(host[:2]):
+        fmt = wq.WQ_FMT_NVFP4_TILED if f == "nvfp4" else wq.WQ_FMT_FP8ROW_TILED
+        if wq.wq_gemm_split(fmt, d.M, d.K) == wq.wq_gemm_split(fmt, d.M, d.K, 2):
+            y1 = run_tiled(wq, d, 8) if f == "nvfp4" else run_fp8_tiled(wq, d, 8)
+            assert np.array_equal(y1.view(np.uint32), outs[8][i].view(np.uint32)), "%s M=%d" % (f, d.M)
+        else:
+            print("%s: single-matrix split %s differs from the blocked split: bitwise comparison skipped"
+                  % (f, wq.wq_gemm_split(fmt, d.M, d.K)), flush=True)
