@@ -147,28 +147,87 @@ def read_traffic():
 
 # ---- CPU baseline ----------------------------------------------------------------
 
-def cpu_baseline(wl, host, budget_s=12.0, max_layers=8):
-    """The oracle, as it is, on the first layers of the same pass: every
-    matrix of layer l at N = 2, 4 and 8, layer after layer until `budget_s`
-    seconds of CPU time have been spent (at most `max_layers` layers)."""
+def host_cpu():
+    """The host's logical CPU count, the CPUs this process may run on, and
+    the CPU model name as lscpu reports it (falling back to /proc/cpuinfo)."""
+    model = None
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    if model is None and os.path.exists("/proc/cpuinfo"):
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = None
+    return {"nproc": os.cpu_count(), "cpus_allowed": allowed, "model": model}
+
+
+def cpu_baseline(wl, host, budget_s=12.0, max_layers=8, one_thread_stride=16):
+    """The oracle, as it is, on the first layers of the same pass.
+
+    All threads: every matrix of layer l at N = 2, 4 and 8, layer after layer
+    until `budget_s` seconds have been spent (at most `max_layers` layers);
+    the time per N, scaled to the pass's layers, is the oracle's time per
+    pass at that N.  One thread: every `one_thread_stride`-th row of layer
+    0's four matrices at N = 2, 4 and 8 (the oracle's cost is linear in the
+    rows it computes)."""
     import oracle
+    t_n = {N: 0.0 for N in N_CYCLE}
+    b_n = {N: 0 for N in N_CYCLE}
     t0 = time.perf_counter()
-    nbytes, layers = 0, 0
+    layers = 0
     while layers < max_layers:
         for j in range(4):
             i = 4 * layers + j
             d = host[i]
+            s = wl.matrices[i]
             for N in N_CYCLE:
+                ta = time.perf_counter()
                 oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N])
-                s = wl.matrices[i]
-                nbytes += s.M * s.K // 2 + s.M * s.K // 16 + 2 * N * s.K + 4 * N * s.M + 4
+                t_n[N] += time.perf_counter() - ta
+                b_n[N] += s.M * s.K // 2 + s.M * s.K // 16 + 2 * N * s.K + 4 * N * s.M + 4
         layers += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "FP64 oracle (C, OpenMP) on all rows of layers 0..%d (%d matrices) at N=2,4,8: %.3f GB "
-                      "algorithmic in %.1f s" % (layers - 1, 4 * layers, nbytes / 1e9, dt)}
+    dt = sum(t_n.values())
+    nbytes = sum(b_n.values())
+    threads = oracle.num_threads()
+    pass_layers = len(wl.matrices) // 4
+    per_n = {str(N): {"us_per_pass": t_n[N] / layers * pass_layers * 1e6, "gbps": b_n[N] / t_n[N] / 1e9}
+             for N in N_CYCLE}
+    # one thread, on a row sample of layer 0
+    oracle.set_num_threads(1)
+    try:
+        t1, b1 = 0.0, 0
+        for j in range(4):
+            d, s = host[j], wl.matrices[j]
+            rows = np.arange(0, s.M, one_thread_stride)
+            for N in N_CYCLE:
+                ta = time.perf_counter()
+                oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x[:N], rows=rows)
+                t1 += time.perf_counter() - ta
+                b1 += rows.size * (s.K // 2 + s.K // 16 + 4 * N) + 2 * N * s.K + 4
+        one = {"value": b1 / t1 / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+               "sample": "every %dth row of layer 0's 4 matrices at N=2,4,8: %.4f GB algorithmic in %.1f s"
+                         % (one_thread_stride, b1 / 1e9, t1)}
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "FP64 oracle (C, OpenMP, %d threads) on all rows of layers 0..%d (%d matrices) at N=2,4,8: "
+                      "%.3f GB algorithmic in %.1f s; us_per_pass scales the per-layer time to %d layers"
+                      % (threads, layers - 1, 4 * layers, nbytes / 1e9, dt, pass_layers),
+            "host": host_cpu(), "per_n": per_n, "one_thread": one,
+            "speedup_one_to_all": (nbytes / dt) / (b1 / t1)}
 
 
 # ---- the cpu_baseline leg's comparisons ------------------------------------------
@@ -369,7 +428,7 @@ def single_products(wq, torch, stream, probe_gbps, check_rows=2048):
             us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
             nbytes = matrix_bytes(wl.fmt, M, K, N)
             row = {"workload": ci, "name": wl.name, "N": N, "layout": layout, "split": list(wq.wq_gemm_split(fmt, M, K)),
-                   "us": us, "gbps": nbytes / us / 1e3, "pct_of_8TBps": 100 * nbytes / us / 1e3 / PEAK_GBPS,
+                   "calls": 3 + reps, "us": us, "gbps": nbytes / us / 1e3, "pct_of_8TBps": 100 * nbytes / us / 1e3 / PEAK_GBPS,
                    "pct_of_probe": 100 * nbytes / us / 1e3 / probe_gbps, "copies": copies}
             own = N == wl.N
             rows = np.arange(M) if (own and M <= check_rows) else np.unique(
@@ -429,7 +488,8 @@ def head_accept_rows(wq, torch, stream, wl, d, tiled, nt, rs, x8, probe_gbps):
         tk, a = tokens.cpu().numpy(), int(acc.cpu().numpy()[0])
         lgn = logits.cpu().numpy()
         row = {"workload": 4, "name": "greedy acceptance fused on the fp8-row head 151936x5120",
-               "N": N, "layout": "tiled", "logits_written": with_logits, "us": us,
+               "N": N, "layout": "accept+logits" if with_logits else "accept", "logits_written": with_logits,
+               "calls": 3 + reps + (0 if with_logits else 1), "us": us,
                "gbps": nbytes / us / 1e3, "pct_of_8TBps": 100 * nbytes / us / 1e3 / PEAK_GBPS,
                "pct_of_probe": 100 * nbytes / us / 1e3 / probe_gbps, "accepted": a, "parity_ok": None,
                "max_err_over_bound": 0.0, "rows_checked": 0}
@@ -586,7 +646,7 @@ def chain_bytes(D, F, N, layers):
     return per * layers
 
 
-def chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=48, reps=5):
+def chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=48, reps=5, single_launch=True):
     """The verify pass as chained MLP layers (wq_mlp_chain_*): each of the
     pass's layers applies RMSNorm, gate/up (rows 0..F-1 and F..2F-1 of its
     gate_up matrix), SwiGLU and down to the residual stream of the N verify
@@ -643,7 +703,7 @@ def chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=48,
         torch.cuda.synchronize()
         graph_us = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
         single_us = None
-        if plan.grid_chain > 0:
+        if single_launch and plan.grid_chain > 0:
             wq.wq_mlp_chain_launch_persistent(plan, stream)
             for e0, e1 in ev:
                 h.copy_(h0)
@@ -661,7 +721,10 @@ def chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=48,
                         "single_launch_us": single_us,
                         "pct_of_8TBps_single_launch": (100 * nb / single_us / 1e3 / PEAK_GBPS) if single_us else None,
                         "launches": 3 * layers + 1, "down_k_chunks": nc}
-        del graph, ws, plan
+        # the graph and its capture stream are released (and the device idle)
+        # before the next N's buffers are made
+        torch.cuda.synchronize()
+        del graph, side, ws, plan
 
     # layer 0 at N = 8 against the oracle (sampled rows of s and h)
     N = 8
@@ -688,7 +751,370 @@ def chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps, check_rows=48,
     return row
 
 
+# ---- rocprofv3 summaries (profiles/) ----------------------------------------------
+# `bench.py --summarize-rocprof KIND --rocprof-dir DIR [--rocprof-dir DIR2] [--bench-log LOG] --out FILE`
+# turns the CSV output of a profiled bench.py run into the text committed
+# under profiles/.  The profiled commands are written into each summary.
+
+PROF_CMD = {
+    "dense": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/kt -o kt -- python3 bench.py "
+             "--steps 30 --warmup 3 --no-cpu-baseline --no-single --no-chain --check-rows 2 --workers 0",
+    "single": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/kts -o kts -- python3 bench.py "
+              "--only-single --no-cpu-baseline",
+    "chain": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktc -o ktc -- python3 bench.py "
+             "--steps 3 --warmup 1 --no-cpu-baseline --no-single --no-chain-single --check-rows 1 --workers 0",
+    "traffic_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- python3 "
+                     "bench.py --steps 6 --warmup 0 --no-cpu-baseline --no-single --no-chain --check-rows 1 --workers 0",
+    "traffic_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- python3 "
+                     "bench.py --steps 6 --warmup 0 --no-cpu-baseline --no-single --no-chain --check-rows 1 --workers 0",
+    "single_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcs_fetch -o fetch -- python3 "
+                    "bench.py --only-single --no-cpu-baseline",
+    "single_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcs_write -o write -- python3 "
+                    "bench.py --only-single --no-cpu-baseline",
+}
+
+
+def _kernel_name(raw):
+    import re
+    n = re.sub(r"^void ", "", raw)
+    n = re.sub(r"\(anonymous namespace\)::", "", n)
+    n = re.sub(r"\((?:[^()]|\([^()]*\))*\)$", "", n).strip()
+    return n
+
+
+def _rocprof_csv(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no %s files under %s" % (suffix, d))
+    return rows
+
+
+def _trace(d):
+    """Kernel dispatches of a --kernel-trace run: (start ns, end ns, name), in start order."""
+    out = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _kernel_name(r["Kernel_Name"]))
+           for r in _rocprof_csv(d, "kernel_trace.csv")]
+    return sorted(out)
+
+
+def _counters(d):
+    """Per-dispatch counter values of a --pmc run, in dispatch order: [(name, value)]."""
+    rows = _rocprof_csv(d, "counter_collection.csv")
+    key = "Dispatch_Id" if "Dispatch_Id" in rows[0] else None
+    rows.sort(key=lambda r: int(r[key]) if key else 0)
+    return [(_kernel_name(r["Kernel_Name"]), float(r["Counter_Value"])) for r in rows]
+
+
+def _stats(v):
+    import statistics
+    return len(v), statistics.mean(v), statistics.median(v), min(v), max(v)
+
+
+def _bench_json(path):
+    with open(path) as f:
+        lines = [l for l in f if l.startswith("{")]
+    if not lines:
+        raise SystemExit("no JSON line in %s" % path)
+    return json.loads(lines[-1])
+
+
+def _summary_cmd(kind, args):
+    extra = "".join(" --rocprof-dir %s" % d for d in args.rocprof_dir)
+    if args.bench_log:
+        extra += " --bench-log %s" % args.bench_log
+    return "python3 bench.py --summarize-rocprof %s%s --out %s" % (kind, extra, args.out or "-")
+
+
+def summarize_dense(args):
+    """Kernel trace of the dense pass: the timed region's launches per N
+    (the launches longer than 1 ms after the warm-up ones), and every
+    dispatch of the run."""
+    rows = _trace(args.rocprof_dir[0])
+    bl = _bench_json(args.bench_log)
+    dense = [(s, e, n) for s, e, n in rows if n.startswith("wq::stream_kernel<") and n.endswith(", 4>")
+             and (e - s) > 1e6]
+    steps, warm = bl["steps"], bl["warmup"]
+    timed = dense[warm:warm + steps]
+    L = ["# Kernel trace of the dense verify pass (64 layers, NVFP4, N cycled 2/4/8), MI355X", "#",
+         "# commands (from the repository root, after `export TMPDIR=/tmp`):",
+         "#   " + PROF_CMD["dense"] + " > gpurun_out/prof_kt.log",
+         "#   " + _summary_cmd("dense", args), "#",
+         "# stream_kernel<N, 4> is the tiled verify pass (the timed path of bench.py; one launch per pass, the",
+         "# 64 down projections computed in LDS blocks, no reduction launch); stream_kernel<N, 0> the plain",
+         "# row-major pass (reported as plain_layout) with its split-K reduce_kernel; stream_kernel_dyn the pass",
+         "# with N read on the device (per_n_device_count); probe_read_kernel<false> / <true> the read probe and",
+         "# the read-with-writes probe.  Durations in microseconds.", "",
+         "timed region of bench.py (the %d steps between its two synchronizations, %d per N):" % (steps, steps // 3),
+         "%-36s %7s %12s %12s %12s %12s %9s" % ("kernel", "calls", "avg_us", "median_us", "min_us", "max_us",
+                                               "%8TB_avg")]
+    wl = inputs.workload(3)
+    for N in N_CYCLE:
+        v = [(e - s) / 1e3 for s, e, n in timed if n == "wq::stream_kernel<%d, 4>" % N]
+        st = _stats(v)
+        L.append("%-36s %7d %12.1f %12.1f %12.1f %12.1f %9.1f" % (("wq::stream_kernel<%d, 4>" % N,) + st + (
+            100 * algorithmic_bytes(wl, N) / (st[1] * 1e3) / PEAK_GBPS,)))
+    v = [(e - s) / 1e3 for s, e, n in timed]
+    tot = sum(algorithmic_bytes(wl, int(n.split("<")[1].split(",")[0])) for s, e, n in timed)
+    L.append("%-36s %7d %12.1f %12.1f %12.1f %12.1f %9.1f" % (("all timed launches",) + _stats(v) + (
+        100 * tot / (sum(v) * 1e3) / PEAK_GBPS,)))
+    L += ["", "bench.py's own figures for the same run (HIP events on the launch stream):",
+          "  roofline.avg_launch_us = %.1f; per_n us_per_pass_mean = %s" % (
+              bl["roofline"]["avg_launch_us"],
+              ", ".join("N=%s %.1f" % (k, x["us_per_pass_mean"]) for k, x in bl["per_n"].items())), "",
+          "every dispatch of the run:",
+          "%-36s %7s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "median_us", "min_us", "max_us")]
+    keep, order = {}, []
+    for s, e, n in rows:
+        if not n.startswith("wq::"):
+            continue
+        if n not in keep:
+            order.append(n)
+        keep.setdefault(n, []).append((e - s) / 1e3)
+    for n in order:
+        L.append("%-36s %7d %12.1f %12.1f %12.1f %12.1f" % ((n[:36],) + _stats(keep[n])))
+    return "\n".join(L) + "\n"
+
+
+def _single_groups(rows, bl):
+    """Assign the single products' dispatches to bench rows: each row made
+    `calls` calls, back to back, in the order of the JSON; a call is one
+    stream kernel, then (split products) a reduce_kernel or (acceptance) an
+    accept_kernel."""
+    main = []
+    for s, e, n in rows:
+        if n.startswith("wq::stream_kernel<"):
+            main.append([n, (e - s) / 1e3, 0.0])
+        elif n in ("wq::reduce_kernel", "wq::accept_kernel") and main:
+            main[-1][2] += (e - s) / 1e3
+    out, i = [], 0
+    for r in bl["single_products"]:
+        grp = main[i:i + r["calls"]]
+        i += r["calls"]
+        names = {g[0] for g in grp}
+        if len(grp) != r["calls"] or len(names) != 1:
+            raise SystemExit("dispatches do not match the bench rows at %s N=%d %s" % (r["name"], r["N"], r["layout"]))
+        out.append((r, names.pop(), [g[1] for g in grp], [g[2] for g in grp]))
+    if i != len(main):
+        raise SystemExit("%d stream-kernel dispatches left over" % (len(main) - i))
+    return out
+
+
+def _row_bytes(r):
+    wl = inputs.workload(r["workload"])
+    M, K = wl.matrices[0].M, wl.matrices[0].K
+    nb = matrix_bytes(wl.fmt, M, K, r["N"])
+    if r["layout"] == "accept":
+        nb -= 4 * r["N"] * M
+    return nb
+
+
+def summarize_single(args):
+    """Kernel trace of the single products (--only-single run)."""
+    import statistics
+    rows = _trace(args.rocprof_dir[0])
+    bl = _bench_json(args.bench_log)
+    L = ["# Kernel trace of the single products (workloads 0, 1, 2, 4), MI355X", "#",
+         "# commands (from the repository root, after `export TMPDIR=/tmp`):",
+         "#   " + PROF_CMD["single"] + " > gpurun_out/prof_kts.log",
+         "#   " + _summary_cmd("single", args), "#",
+         "# Each row: one (workload, layout, N) run of back-to-back calls over rotated weight copies (> 1 GiB);",
+         "# layout accept: greedy acceptance fused on the tiled FP8 head (wq_head_accept), without / with logits;",
+         "# us = median stream-kernel duration plus median second kernel (reduce or accept) duration;",
+         "# GB/s = algorithmic bytes / us; events_us = bench.py's HIP-event median per call (launch included).", "",
+         "%-44s %-14s %2s %-27s %6s %9s %8s %9s %8s %6s" % ("workload", "layout", "N", "kernel", "calls", "stream_us",
+                                                         "2nd_us", "events_us", "GB/s", "%8TB")]
+    for r, name, d, d2 in _single_groups(rows, bl):
+        sd, s2 = statistics.median(d), statistics.median(d2)
+        us, nb = sd + s2, _row_bytes(r)
+        L.append("%-44s %-14s %2d %-27s %6d %9.2f %8.2f %9.2f %8.0f %6.1f" % (
+            r["name"][:44], r["layout"], r["N"], name[:27], len(d), sd, s2, r["us"], nb / us / 1e3,
+            100 * nb / us / 1e3 / PEAK_GBPS))
+    return "\n".join(L) + "\n"
+
+
+def _copy_scale(c):
+    v = [x for n, x in c if n == "wq::probe_copy_kernel"]
+    if not v:
+        raise SystemExit("no probe_copy_kernel dispatch in the counter run")
+    return (1 << 30) / (v[0] * 1024)
+
+
+def summarize_traffic(args):
+    """FETCH_SIZE and WRITE_SIZE of the dense pass's kernels, scaled by the
+    same counters on a 1 GiB copy."""
+    import statistics
+    fe, wr = _counters(args.rocprof_dir[0]), _counters(args.rocprof_dir[1])
+    fs, ws = _copy_scale(fe), _copy_scale(wr)
+    wl = inputs.workload(3)
+    by = lambda c, k: [x for n, x in c if n == k]  # noqa: E731
+    L = ["# HBM traffic of the tiled-NVFP4 verify pass kernel, from rocprofv3 counters on MI355X", "#",
+         "# commands (one counter per run, from the repository root, after `export TMPDIR=/tmp`):",
+         "#   " + PROF_CMD["traffic_fetch"], "#   " + PROF_CMD["traffic_write"], "#   " + _summary_cmd("traffic", args),
+         "#", "# Scale: the same counters on wq_probe_copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB):",
+         "#   FETCH_SIZE read %.1f KiB -> factor %.4f;  WRITE_SIZE read %.1f KiB -> factor %.4f" % (
+             (1 << 30) / fs / 1024, fs, (1 << 30) / ws / 1024, ws),
+         "# Per-dispatch values below are KiB as counted (mean over the run's dispatches), then bytes after scaling.",
+         ""]
+    tot = []
+    for N in N_CYCLE:
+        k = "wq::stream_kernel<%d, 4>" % N
+        f, w = statistics.mean(by(fe, k)), statistics.mean(by(wr, k))
+        b = f * 1024 * fs + w * 1024 * ws
+        a = algorithmic_bytes(wl, N)
+        tot.append(b)
+        L.append("N=%d: FETCH_SIZE %.0f KiB (x%.3f) + WRITE_SIZE %.0f KiB (x%.3f) = %.0f bytes; algorithmic %d bytes; "
+                 "ratio %.4f" % (N, f, fs, w, ws, b, a, b / a))
+        kp = "wq::stream_kernel<%d, 0>" % N
+        if by(fe, kp) and by(wr, kp):
+            bp = statistics.mean(by(fe, kp)) * 1024 * fs + statistics.mean(by(wr, kp)) * 1024 * ws
+            L.append("     plain layout stream_kernel<%d, 0>: %.0f bytes (ratio %.4f; its reduce_kernel launches "
+                     "are extra)" % (N, bp, bp / a))
+    L += ["", "kernel_source_sha256_16 = %s" % kernel_source_hash(), "fetch_scale = %.6f" % fs,
+          "write_scale = %.6f" % ws, "hbm_bytes_per_launch_mean = %.0f" % statistics.mean(tot)]
+    return "\n".join(L) + "\n"
+
+
+def summarize_single_traffic(args):
+    """FETCH_SIZE and WRITE_SIZE of every single-product call (--only-single
+    runs), per bench row: the median bytes per call against the algorithmic
+    bytes.  A ratio under 0.98 means some weight bytes came from a cache."""
+    import statistics
+    bl = _bench_json(args.bench_log)
+    fe, wr = _counters(args.rocprof_dir[0]), _counters(args.rocprof_dir[1])
+    fs, ws = _copy_scale(fe), _copy_scale(wr)
+
+    def per_row(c):
+        seq = []
+        for n, x in c:
+            if n.startswith("wq::stream_kernel<"):
+                seq.append([n, x])
+            elif n in ("wq::reduce_kernel", "wq::accept_kernel") and seq:
+                seq[-1][1] += x
+        out, i = [], 0
+        for r in bl["single_products"]:
+            out.append([x for _, x in seq[i:i + r["calls"]]])
+            i += r["calls"]
+        if i != len(seq):
+            raise SystemExit("%d stream-kernel dispatches left over" % (len(seq) - i))
+        return out
+
+    pf, pw = per_row(fe), per_row(wr)
+    L = ["# HBM traffic of the single products (workloads 0, 1, 2, 4), from rocprofv3 counters on MI355X", "#",
+         "# commands (one counter per run, from the repository root, after `export TMPDIR=/tmp`):",
+         "#   " + PROF_CMD["single_fetch"], "#   " + PROF_CMD["single_write"],
+         "#   " + _summary_cmd("single-traffic", args), "#",
+         "# Scale: FETCH_SIZE x%.4f, WRITE_SIZE x%.4f (the counters on wq_probe_copy of exactly 1 GiB)." % (fs, ws),
+         "# Per call (stream kernel plus its reduce or accept kernel, median over the row's calls): bytes after",
+         "# scaling.  ratio = (fetch + write) / algorithmic bytes; a ratio under 0.98 is flagged (weights served",
+         "# from a cache: the rotation over copies did not defeat the 256 MB last-level cache).", "",
+         "%-44s %-14s %2s %12s %12s %14s %7s %s" % ("workload", "layout", "N", "fetch_B", "write_B", "algorithmic_B",
+                                                   "ratio", "flag")]
+    for r, f, w in zip(bl["single_products"], pf, pw):
+        fb, wb = statistics.median(f) * 1024 * fs, statistics.median(w) * 1024 * ws
+        nb = _row_bytes(r)
+        ratio = (fb + wb) / nb
+        L.append("%-44s %-14s %2d %12.0f %12.0f %14d %7.4f %s" % (r["name"][:44], r["layout"], r["N"], fb, wb, nb,
+                                                                 ratio, "CACHED" if ratio < 0.98 else ""))
+    return "\n".join(L) + "\n"
+
+
+def summarize_chain(args):
+    """Kernel trace of the chained MLP rows."""
+    rows = _trace(args.rocprof_dir[0])
+    L = ["# Kernel trace of the chained MLP pass (64 layers: RMSNorm + gate/up 34816x5120 + SwiGLU, down 5120x17408,",
+         "# residual) in bench.py's chained_mlp rows, MI355X", "#",
+         "# commands (from the repository root, after `export TMPDIR=/tmp`):",
+         "#   " + PROF_CMD["chain"] + " > gpurun_out/prof_ktc.log", "#   " + _summary_cmd("chain", args), "#",
+         "# stream_kernel<N, 6>: gate/up with RMSNorm staging and SwiGLU epilogue (100.3 MB of weights per layer);",
+         "# stream_kernel<N, 7>: down, K split in chunks (50.1 MB per layer); chain_reduce_kernel: residual update",
+         "# and sums of squares (once more per launch for the first layer's norm).  The rows include the warm-up,",
+         "# eager, graph-replay runs and the layer-0 check.  The single cooperative launch (chain_kernel<N>) is",
+         "# left out of profiled runs (--no-chain-single); bench.py times it with HIP events.  Microseconds.", "",
+         "%-40s %7s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "median_us", "min_us", "max_us")]
+    keep, order = {}, []
+    for s, e, n in rows:
+        if not (n.startswith("wq::stream_kernel<") and (n.endswith(", 6>") or n.endswith(", 7>"))
+                or n.startswith("wq::chain")):
+            continue
+        if n not in keep:
+            order.append(n)
+        keep.setdefault(n, []).append((e - s) / 1e3)
+    for n in order:
+        L.append("%-40s %7d %12.1f %12.1f %12.1f %12.1f" % ((n[:40],) + _stats(keep[n])))
+    return "\n".join(L) + "\n"
+
+
+SUMMARIES = {"dense": summarize_dense, "single": summarize_single, "traffic": summarize_traffic,
+             "single-traffic": summarize_single_traffic, "chain": summarize_chain}
+
+
 # ---- main ------------------------------------------------------------------------
+
+def run_probes(wq, torch, stream):
+    """The read probe (attainable read rate), the read-with-writes probe (the
+    price of an output byte) and one copy of exactly 1 GiB (the scale of the
+    byte counters in profiled runs)."""
+    dev = torch.device("cuda:0")
+    probe_buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    probe_buf.fill_(1)
+    sink = torch.empty(wq.wq_probe_sink_words(), dtype=torch.int32, device=dev)
+    for _ in range(2):
+        wq.wq_probe_read(probe_buf, sink, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        wq.wq_probe_read(probe_buf, sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    probe_gbps = 5 * probe_buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # the same read stream with about 1% of its bytes written as scattered
+    # 256-byte write-through stores (the verify pass's outputs at N = 8 are
+    # 0.9% of its bytes): what an output byte costs in read time
+    every_kb = 96
+    wdst = torch.empty(wq.wq_probe_read_write_bytes(probe_buf.numel(), every_kb), dtype=torch.uint8, device=dev)
+    wq.wq_probe_read_write(probe_buf, wdst, every_kb, sink, stream)
+    e0.record(stream)
+    for _ in range(5):
+        wq.wq_probe_read_write(probe_buf, wdst, every_kb, sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_rw = e0.elapsed_time(e1) * 1e-3 / 5
+    t_r = probe_buf.numel() / (probe_gbps * 1e9)
+    write_probe = {"every_kb_read": every_kb, "bytes_read": probe_buf.numel(), "bytes_written": wdst.numel(),
+                   "read_only_gbps": probe_gbps, "with_writes_read_gbps": probe_buf.numel() / t_rw / 1e9,
+                   "us_per_mb_written": (t_rw - t_r) * 1e6 / (wdst.numel() / 1e6),
+                   "read_bytes_lost_per_byte_written": (t_rw - t_r) * probe_gbps * 1e9 / wdst.numel()}
+    del wdst
+    copy_dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    wq.wq_probe_copy(probe_buf[: 1 << 30], copy_dst, stream)
+    torch.cuda.synchronize()
+    del probe_buf, copy_dst
+    torch.cuda.empty_cache()
+    return probe_gbps, write_probe
+
+
+def only_single(args):
+    """--only-single: the probes and the single products, nothing else (the
+    run profiled for the single products' kernel trace and byte counters)."""
+    import torch
+    from fp8_weight_streaming_amd import wq
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    probe_gbps, write_probe = run_probes(wq, torch, stream)
+    singles = single_products(wq, torch, stream, probe_gbps)
+    ok = None
+    if not args.no_cpu_baseline:
+        ok = run_oracle_checks()
+    print(json.dumps({"single_products": singles, "probe_read_gbps": probe_gbps, "probe_write_cost": write_probe,
+                      "parity_ok": ok}))
+    if ok is False:
+        print("[bench] PARITY FAILED", file=sys.stderr)
+        sys.exit(1)
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -699,15 +1125,38 @@ def main():
     ap.add_argument("--check-rows", type=int, default=32, help="sampled rows per matrix checked against the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the single-product workloads 0, 1, 2, 4")
+    ap.add_argument("--only-single", action="store_true",
+                    help="run only the probes and the single products (profiled runs of the single products)")
     ap.add_argument("--no-chain", action="store_true", help="skip the chained MLP pass")
+    ap.add_argument("--no-chain-single", action="store_true",
+                    help="skip the chain's single cooperative launch (kept out of rocprofv3 runs)")
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--summarize-rocprof", metavar="KIND", choices=sorted(SUMMARIES),
+                    help="write a profiles/ summary from rocprofv3 CSV output instead of benchmarking: " +
+                         ", ".join(sorted(SUMMARIES)))
+    ap.add_argument("--rocprof-dir", action="append", default=[],
+                    help="rocprofv3 output directory (twice for the traffic summaries: FETCH_SIZE, then WRITE_SIZE)")
+    ap.add_argument("--bench-log", help="stdout of the profiled bench.py run (its JSON line)")
+    ap.add_argument("--out", help="summary file to write")
     args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        text = SUMMARIES[args.summarize_rocprof](args)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        print(text, end="")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (the matrices of a verify pass are "
               "independent and would shard by rows or by matrix with no exchange). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.only_single:
+        only_single(args)
+        return
 
     wl = inputs.workload(3, layers=args.layers)
     t_gen = time.perf_counter()
@@ -756,41 +1205,7 @@ def main():
     plans = {N: p for N, (p, _) in plans_t.items()}
     torch.cuda.synchronize()
 
-    # attainable read rate (probe) and a copy of known size (counter scale)
-    probe_buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
-    probe_buf.fill_(1)
-    sink = torch.empty(wq.wq_probe_sink_words(), dtype=torch.int32, device=dev)
-    for _ in range(2):
-        wq.wq_probe_read(probe_buf, sink, stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(5):
-        wq.wq_probe_read(probe_buf, sink, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    probe_gbps = 5 * probe_buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    # the same read stream with about 1% of its bytes written as scattered
-    # 256-byte write-through stores (the verify pass's outputs at N = 8 are
-    # 0.9% of its bytes): what an output byte costs in read time
-    every_kb = 96
-    wdst = torch.empty(wq.wq_probe_read_write_bytes(probe_buf.numel(), every_kb), dtype=torch.uint8, device=dev)
-    wq.wq_probe_read_write(probe_buf, wdst, every_kb, sink, stream)
-    e0.record(stream)
-    for _ in range(5):
-        wq.wq_probe_read_write(probe_buf, wdst, every_kb, sink, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_rw = e0.elapsed_time(e1) * 1e-3 / 5
-    t_r = probe_buf.numel() / (probe_gbps * 1e9)
-    write_probe = {"every_kb_read": every_kb, "bytes_read": probe_buf.numel(), "bytes_written": wdst.numel(),
-                   "read_only_gbps": probe_gbps, "with_writes_read_gbps": probe_buf.numel() / t_rw / 1e9,
-                   "us_per_mb_written": (t_rw - t_r) * 1e6 / (wdst.numel() / 1e6),
-                   "read_bytes_lost_per_byte_written": (t_rw - t_r) * probe_gbps * 1e9 / wdst.numel()}
-    del wdst
-    copy_dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    wq.wq_probe_copy(probe_buf[: 1 << 30], copy_dst, stream)
-    torch.cuda.synchronize()
-    del probe_buf, copy_dst
+    probe_gbps, write_probe = run_probes(wq, torch, stream)
 
     # warmup
     for i in range(args.warmup):
@@ -833,7 +1248,8 @@ def main():
     traffic, traffic_kv = read_traffic()
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / PEAK_GBPS, "traffic": traffic,
-                "kernel": "wq::stream_kernel<N, tiled-NVFP4 mode> + wq::reduce_kernel (one verify pass)",
+                "kernel": "wq::stream_kernel<N, 4> (the tiled verify pass: one launch per pass; its split "
+                          "matrices are computed in LDS blocks, so no reduction launch follows)",
                 "avg_launch_us": kernel_s / steps * 1e6,
                 "algorithmic_bytes_per_launch_mean": total_bytes / steps,
                 "traffic_gbps": (traffic / (kernel_s / steps) / 1e9) if traffic else None,
@@ -874,7 +1290,8 @@ def main():
     device_n = device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n)
     chained = None
     if not args.no_chain:
-        chained = chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps)
+        chained = chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps,
+                             single_launch=not args.no_chain_single)
     draft = None
     singles = quant = None
     if not args.no_single:
@@ -911,16 +1328,18 @@ def main():
                    "weight_bytes_per_pass": sum(s.M * s.K // 2 + s.M * s.K // 16 for s in wl.matrices),
                    "pct_of_8TBps": 100 * value / PEAK_GBPS,
                    "us_per_pass": wall_s / steps * 1e6},
-        "per_n": per_n,
+        # the long secondary rows first; the per-N figures, the parity
+        # check, the CPU baseline and the roofline close the line
         "plain_layout": plain,
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "parity": parity,
         "per_n_device_count": device_n,
         "draft_step": draft,
         "chained_mlp": chained,
         "single_products": singles,
         "quantizers": quant,
+        "per_n": per_n,
+        "parity": parity,
+        "cpu_baseline": cpu,
+        "roofline": roofline,
     }
     print(json.dumps(out))
     if not ok:

@@ -64,6 +64,8 @@ def _load():
                                        P, ctypes.c_int, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -86,6 +88,11 @@ def bf16(bits: int) -> float:
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's later parallel loops (n >= 1)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _c(arr, dtype):

@@ -150,3 +150,9 @@ int oracle_num_threads(void) {
   }
   return n;
 }
+
+/* Sets the OpenMP thread count of later parallel regions (n >= 1); used
+ * only to time the oracle on one thread against all of them. */
+void oracle_set_num_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+}
