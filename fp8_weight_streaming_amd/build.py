@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwq.so")
-SOURCES = ["wq_kernels.hip", "wq_tile.hip", "wq_quant.hip", "wq_probe.hip", "wq_api.cpp"]
+SOURCES = ["wq_kernels.hip", "wq_tile.hip", "wq_quant.hip", "wq_probe.hip", "wq_noalloc.hip", "wq_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

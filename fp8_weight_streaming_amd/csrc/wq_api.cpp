@@ -185,9 +185,7 @@ DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x
 
 wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x, float* y, int M, int K,
                int N, void* ws, size_t ws_bytes, void* stream) {
-  wq_status st = check_shape(fmt, M, K, N);
-  if (st != WQ_SUCCESS) return st;
-  st = check_ptrs(fmt, w, s, x, y);
+  wq_status st = check_gemm_args(fmt, w, s, x, y, M, K, N);
   if (st != WQ_SUCCESS) return st;
   if (ws && !aligned16(ws)) return WQ_ERROR_MISALIGNED;
   const int cus = current_cus();
@@ -526,6 +524,13 @@ void chunk_ranges(int64_t ntiles, int nchunks, int grid, WgRange* out) {
 }
 
 }  // namespace
+
+wq_status check_gemm_args(int fmt, const void* w, const void* s, const void* x, const void* y, int M, int K, int N) {
+  wq_status st = check_shape(fmt, M, K, N);
+  if (st != WQ_SUCCESS) return st;
+  return check_ptrs(fmt, w, s, x, y);
+}
+
 }  // namespace wq
 
 using namespace wq;
@@ -541,6 +546,7 @@ const char* wq_status_string(wq_status s) {
     case WQ_ERROR_WORKSPACE: return "workspace missing or too small";
     case WQ_ERROR_LAUNCH: return "launch failed";
     case WQ_ERROR_DEVICE: return "no usable gfx950 device";
+    case WQ_ERROR_SCRATCH_LIMIT: return "the shape needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }

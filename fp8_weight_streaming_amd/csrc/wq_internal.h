@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wq.h"
+
 namespace wq {
 
 constexpr int kFmtNvfp4 = 0;
@@ -235,6 +237,8 @@ hipError_t launch_chain_persistent(int N, const DevMat* mats, ChainCtl* ctl, flo
                                    int grid, hipStream_t stream);
 // Workgroups of the single-launch chain that fit on the device at once.
 int chain_persistent_blocks_per_cu(int N);
+// Host-side argument checks of the single-matrix products (no HIP call).
+wq_status check_gemm_args(int fmt, const void* w, const void* s, const void* x, const void* y, int M, int K, int N);
 hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t* drafts, int32_t* tokens,
                          int32_t* accepted, hipStream_t stream);
 

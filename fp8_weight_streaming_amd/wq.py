@@ -29,6 +29,7 @@ STATUS_NAMES = {
     4: "WQ_ERROR_WORKSPACE",
     5: "WQ_ERROR_LAUNCH",
     6: "WQ_ERROR_DEVICE",
+    7: "WQ_ERROR_SCRATCH_LIMIT",
 }
 
 
@@ -115,6 +116,8 @@ _lib.wq_nvfp4_untile.restype = _I
 _lib.wq_nvfp4_untile.argtypes = [_P, _I, _I, _P, _P, _P]
 _lib.wq_gemm_nvfp4_tiled.restype = _I
 _lib.wq_gemm_nvfp4_tiled.argtypes = [_P, ctypes.c_float, _P, _P, _I, _I, _I, _P, _S, _P]
+_lib.wq_gemm_nvfp4_tiled_noalloc.restype = _I
+_lib.wq_gemm_nvfp4_tiled_noalloc.argtypes = [_P, ctypes.c_float, _P, _P, _I, _I, _I, _P]
 _lib.wq_fp8_tiled_bytes.restype = _S
 _lib.wq_fp8_tiled_bytes.argtypes = [_I, _I]
 _lib.wq_fp8_tile.restype = _I
@@ -147,7 +150,8 @@ _lib.wq_mlp_chain_launch.argtypes = [ctypes.POINTER(WqMlpPlan), _P]
 _lib.wq_mlp_chain_launch_persistent.restype = _I
 _lib.wq_mlp_chain_launch_persistent.argtypes = [ctypes.POINTER(WqMlpPlan), _P]
 
-EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
+EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm_nvfp4_tiled",
+            "wq_gemm_nvfp4_tiled_noalloc", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
             "wq_head_accept_workspace_bytes", "wq_head_accept", "wq_quantize_fp8row", "wq_quantize_nvfp4",
             "wq_verify_launch_n", "wq_nvfp4_tile_glu", "wq_mlp_chain_workspace_bytes", "wq_mlp_chain_split",
@@ -256,6 +260,19 @@ def wq_gemm_nvfp4_tiled(tiled, global_scale: float, x, y, M: int, K: int, worksp
     wsb = _nbytes(workspace) if workspace_bytes is None else workspace_bytes
     _check(_lib.wq_gemm_nvfp4_tiled(_ptr(tiled), float(global_scale), _ptr(x), _ptr(y), M, K, N, _ptr(workspace),
                                     wsb, _stream(stream)), "wq_gemm_nvfp4_tiled")
+
+
+def wq_gemm_nvfp4_tiled_noalloc(tiled, global_scale: float, x, y, M: int, K: int, stream=None,
+                                N: Optional[int] = None):
+    """wq_gemm_nvfp4_tiled with its split-K scratch in the library's static
+    device buffer (no workspace argument, nothing allocated)."""
+    if N is None:
+        N = x.shape[0]
+    _check(_lib.wq_gemm_nvfp4_tiled_noalloc(_ptr(tiled), float(global_scale), _ptr(x), _ptr(y), M, K, N,
+                                            _stream(stream)), "wq_gemm_nvfp4_tiled_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20  # WQ_NOALLOC_SCRATCH_BYTES in include/wq.h
 
 
 def wq_gemm_fp8row(w, row_scale, x, y, workspace=None, stream=None, M: Optional[int] = None,

@@ -57,7 +57,9 @@ typedef enum wq_status {
   WQ_ERROR_MISALIGNED = 3,        /* an array pointer not 16-byte aligned */
   WQ_ERROR_WORKSPACE = 4,         /* workspace NULL or smaller than the query returned */
   WQ_ERROR_LAUNCH = 5,            /* the HIP runtime refused a launch or a copy */
-  WQ_ERROR_DEVICE = 6             /* no current HIP device, or not a gfx950 device */
+  WQ_ERROR_DEVICE = 6,            /* no current HIP device, or not a gfx950 device */
+  WQ_ERROR_SCRATCH_LIMIT = 7      /* wq_gemm_nvfp4_tiled_noalloc: the shape needs more scratch than
+                                     the library's static buffer holds */
 } wq_status;
 
 enum { WQ_FMT_NVFP4 = 0, WQ_FMT_FP8ROW = 1, WQ_FMT_NVFP4_TILED = 2, WQ_FMT_FP8ROW_TILED = 3 };
@@ -127,6 +129,23 @@ wq_status wq_nvfp4_untile(const uint8_t* tiled, int M, int K,
 wq_status wq_gemm_nvfp4_tiled(const uint8_t* tiled, float global_scale,
                               const uint16_t* x, float* y, int M, int K, int N,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* wq_gemm_nvfp4_tiled without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split-K partial sums live in a
+ * static device buffer of WQ_NOALLOC_SCRATCH_BYTES inside the library: one
+ * per GPU, located on the first call on that GPU and held until the process
+ * ends.  The call allocates nothing, on the host or the device.
+ * Results are those of wq_gemm_nvfp4_tiled with a workspace, bit for bit.
+ * Errors: as wq_gemm_nvfp4_tiled, plus WQ_ERROR_SCRATCH_LIMIT (nothing
+ * launched) when wq_gemm_workspace_bytes(WQ_FMT_NVFP4_TILED, M, K, N) exceeds
+ * WQ_NOALLOC_SCRATCH_BYTES.  Every call on one GPU shares that GPU's
+ * buffer: calls that may overlap in time on one GPU (different streams, or
+ * threads without ordering) race and give undefined results; calls ordered
+ * on one stream are safe. */
+#define WQ_NOALLOC_SCRATCH_BYTES (4u << 20)
+wq_status wq_gemm_nvfp4_tiled_noalloc(const uint8_t* tiled, float global_scale,
+                                      const uint16_t* x, float* y, int M, int K, int N, void* stream);
 
 /* Row-scaled FP8-E4M3 weights (the card's section "Model": projections and
  * output head stored or re-encoded as FP8 with one scale per output row).

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(wq):
 
 def test_status_strings(wq):
     assert wq.wq_status_string(0) == "success"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert wq.wq_status_string(s) not in ("", "unknown status")
     assert wq.wq_status_string(99) == "unknown status"
 
@@ -254,3 +254,18 @@ def _has_gpu():
         return torch.cuda.device_count() > 0
     except Exception:
         return False
+
+
+def test_noalloc_gemm_argument_errors(wq):
+    # validated like wq_gemm_nvfp4_tiled, before any HIP call
+    lib = wq.lib()
+    INV, SHAPE, MIS = 1, 2, 3
+
+    def na(t=FAKE, x=FAKE, y=FAKE, M=64, K=256, N=4):
+        return lib.wq_gemm_nvfp4_tiled_noalloc(t, 1.0, x, y, M, K, N, 0)
+
+    assert na(t=0) == INV and na(x=0) == INV and na(y=0) == INV
+    assert na(N=0) == INV and na(N=9) == INV and na(M=0) == INV
+    assert na(K=48) == SHAPE and na(M=1 << 30, K=1 << 12) == SHAPE
+    assert na(t=MISALIGNED) == MIS and na(y=MISALIGNED) == MIS
+    assert wq.wq_status_string(7) != "unknown status"
