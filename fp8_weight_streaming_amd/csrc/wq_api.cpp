@@ -126,6 +126,64 @@ Split gemm_split(int fmt, int M, int K, int cus) {
   return best;
 }
 
+// A single tiled product with fewer than kSplitTilesPerCu tiles per CU is
+// computed by split_kernel: K is cut into C chunks of s steps (the last one
+// shorter); the workgroups are shared out among the chunks, each taking an
+// equal share of its chunk's tiles, and each workgroup's steps are cut into
+// one equal piece per wave; with C > 1, every tile's C parts are added in
+// chunk order by the workgroup whose part arrives last.  s is chosen by the
+// bytes the busiest CU moves at N = 8 (the most X): the weights of its run,
+// its X chunk and, for C > 1, the parts written and read (512 bytes each
+// way) plus the arrival round trips at the end (taken as 128 KB of
+// streaming, and 2 KB more per chunk).
+// Nothing depends on N, so neither do the results' bits.
+struct TileSplit {
+  bool ok = false;
+  Split chunks;
+  int grid = 0;
+  int slots = 0;  // LDS slots per wave: the most tiles one wave's piece touches
+};
+
+TileSplit tile_split_plan(int fmt, int M, int K, int cus) {
+  TileSplit p;
+  if (!is_tiled(fmt) || cus <= 0) return p;
+  const int sk = seg_k(fmt);
+  const int64_t T = ceil_div(M, kTileRows);
+  if (T >= (int64_t)kSplitTilesPerCu * cus || T > kSplitMaxTiles) return p;
+  const int64_t S = ceil_div(K, sk);
+  if (T * S >= (1ll << 31)) return p;
+  const double step_bytes = is_nvfp4(fmt) ? (double)kTileBlockBytes : (double)kFp8TileBlockBytes;
+  const int W = kSplitThreads / 64;
+  double best = 1e300;
+  for (int64_t s = 1; s <= std::min<int64_t>(S, kKcMax / sk); ++s) {
+    const int64_t C = ceil_div(S, s);
+    if (C > kSplitChunksMax || ceil_div(S, C) != s) continue;  // the balanced chunking of C only
+    const int64_t sl = S - (C - 1) * s;
+    const int64_t G = std::min<int64_t>(cus, T * C);
+    if (G < C) continue;
+    const int64_t tiles_max = ceil_div(T, G / C);  // a chunk gets at least G / C workgroups
+    const int64_t run_max = tiles_max * s;
+    const double tail = C > 1 ? (double)(T * C) * 1024.0 / (double)G + 131072.0 + 2048.0 * (double)C : 0.0;
+    const int64_t smin = std::min(s, sl);
+    const int64_t slots = ceil_div(ceil_div(run_max, W), smin) + 1;
+    if (tiles_max > kSplitArrivalsMax) continue;
+    if (lds_bytes_for(8) + (uint64_t)W * slots * kSplitPartBytes + kSplitStaticLds > 160u * 1024u) continue;
+    const double cost = (double)run_max * step_bytes + 16.0 * (double)(s * sk) + tail;
+    if (cost < best) {
+      best = cost;
+      p.ok = true;
+      p.chunks = make_split(fmt, M, K, (int)(s * sk));
+      p.grid = (int)G;
+      p.slots = (int)slots;
+    }
+  }
+  return p;
+}
+
+size_t tile_split_bytes(const TileSplit& p) {
+  return kSplitCounterBytes + align_up((size_t)p.chunks.nchunks * p.chunks.ntiles * kSplitPartBytes, kAlign);
+}
+
 // ---- validation ------------------------------------------------------------------
 wq_status check_shape(int fmt, int M, int K, int N) {
   if (fmt != kFmtNvfp4 && fmt != kFmtFp8Row && fmt != kFmtNvfp4Tiled && fmt != kFmtFp8RowTiled)
@@ -162,6 +220,16 @@ size_t split_scratch_bytes(const Split& s, int M, int N) {
   return align_up((size_t)s.nchunks * N * M * sizeof(float), kAlign);
 }
 
+// Workspace of a single product: the split-kernel counters come first in
+// every single product's workspace (they must stay zero between calls, and
+// no other single product writes there), then its own scratch.
+size_t gemm_workspace(int fmt, int M, int K, int N, int cus) {
+  const TileSplit ts = tile_split_plan(fmt, M, K, cus);
+  if (ts.ok) return tile_split_bytes(ts);
+  const size_t part = split_scratch_bytes(gemm_split(fmt, M, K, cus), M, N);
+  return part ? kSplitCounterBytes + part : 0;
+}
+
 DevMat dev_mat(int fmt, const void* w, const void* s, float g, const uint16_t* x, float* y, int M, int K,
                const Split& sp, char* scratch, int N, int64_t unit0) {
   DevMat d{};
@@ -190,10 +258,21 @@ wq_status gemm(int fmt, const void* w, const void* s, float g, const uint16_t* x
   if (ws && !aligned16(ws)) return WQ_ERROR_MISALIGNED;
   const int cus = current_cus();
   if (cus <= 0) return WQ_ERROR_DEVICE;
+  const TileSplit ts = tile_split_plan(fmt, M, K, cus);
+  if (ts.ok) {
+    if (!ws || ws_bytes < tile_split_bytes(ts)) return WQ_ERROR_WORKSPACE;
+    const DevMat one = dev_mat(fmt, w, s, g, x, y, M, K, ts.chunks, nullptr, N, 0);
+    const hipError_t e = launch_split(
+        N, one, static_cast<uint32_t*>(ws), reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCounterBytes),
+        ts.slots, ts.grid, lds_bytes_for(N) + (size_t)(kSplitThreads / 64) * ts.slots * kSplitPartBytes,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+  }
   const Split sp = gemm_split(fmt, M, K, cus);
   const size_t need = split_scratch_bytes(sp, M, N);
-  if (need > 0 && (!ws || ws_bytes < need)) return WQ_ERROR_WORKSPACE;
-  const DevMat one = dev_mat(fmt, w, s, g, x, y, M, K, sp, static_cast<char*>(ws), N, 0);
+  if (need > 0 && (!ws || ws_bytes < kSplitCounterBytes + need)) return WQ_ERROR_WORKSPACE;
+  const DevMat one =
+      dev_mat(fmt, w, s, g, x, y, M, K, sp, need ? static_cast<char*>(ws) + kSplitCounterBytes : nullptr, N, 0);
   const int64_t units = (int64_t)sp.nchunks * sp.ntiles;
   const int grid = (int)std::min<int64_t>(cus, units);
   const int mode = fmt == kFmtFp8Row ? kModeFp8
@@ -555,7 +634,7 @@ size_t wq_gemm_workspace_bytes(int fmt, int M, int K, int N) {
   if (check_shape(fmt, M, K, N) != WQ_SUCCESS) return 0;
   const int cus = current_cus();
   if (cus <= 0) return 0;
-  return split_scratch_bytes(gemm_split(fmt, M, K, cus), M, N);
+  return gemm_workspace(fmt, M, K, N, cus);
 }
 
 wq_status wq_gemm_split(int fmt, int M, int K, int in_verify_pass, int* k_chunk, int* n_chunks) {
@@ -570,6 +649,13 @@ wq_status wq_gemm_split(int fmt, int M, int K, int in_verify_pass, int* k_chunk,
   } else {
     const int cus = current_cus();
     if (cus <= 0) return WQ_ERROR_DEVICE;
+    const TileSplit ts = tile_split_plan(fmt, M, K, cus);
+    if (ts.ok) {
+      // tiles split across waves and workgroups: reported as k_chunk 0
+      *k_chunk = 0;
+      *n_chunks = ts.chunks.nchunks;
+      return WQ_SUCCESS;
+    }
     sp = gemm_split(fmt, M, K, cus);
   }
   *k_chunk = sp.kc;
@@ -727,6 +813,23 @@ wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream) {
   const DevMat none{};
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_stream(plan->N, plan->mode, reinterpret_cast<const DevMat*>(ws),
+                               reinterpret_cast<const WgRange*>(ws + plan->ranges_offset), none, plan->grid,
+                               lds_bytes_for(plan->N) + (size_t)plan->lds_extra, s);
+  if (e == hipSuccess && plan->reduce_runs > 0)
+    e = launch_reduce(reinterpret_cast<const DevMat*>(ws), reinterpret_cast<const ReduceTask*>(ws + plan->reduce_offset),
+                      none, plan->reduce_runs, plan->N, s);
+  return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
+}
+
+wq_status wq_verify_launch_valu(const wq_verify_plan* plan, void* stream) {
+  if (!plan || !plan->workspace || plan->N < 1 || plan->N > 8 || plan->grid < 1 || plan->count < 1 ||
+      plan->mode != kModeTiled || plan->ranges_offset >= plan->workspace_bytes || plan->reduce_runs < 0 ||
+      (plan->reduce_runs > 0 && plan->reduce_offset >= plan->workspace_bytes) || !lds_extra_ok(*plan))
+    return WQ_ERROR_INVALID_VALUE;
+  const char* ws = static_cast<const char*>(plan->workspace);
+  const DevMat none{};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_stream(plan->N, kModeTiledValu, reinterpret_cast<const DevMat*>(ws),
                                reinterpret_cast<const WgRange*>(ws + plan->ranges_offset), none, plan->grid,
                                lds_bytes_for(plan->N) + (size_t)plan->lds_extra, s);
   if (e == hipSuccess && plan->reduce_runs > 0)

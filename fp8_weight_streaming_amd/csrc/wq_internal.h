@@ -196,14 +196,15 @@ constexpr int kModeTiledArgmax = 5;   // one tiled matrix, greedy keys per workg
 // ring, to fit their registers) let every tile of a workgroup stream at once.
 constexpr int kModeTiledGlu = 6;      // tiled NVFP4 gate/up with RMSNorm staging and SwiGLU outputs
 constexpr int kModeTiledWide = 7;     // tiled NVFP4 / FP8 at 16 waves, static ranges only
+constexpr int kModeTiledValu = 8;     // kModeTiled with the NVFP4 steps on the vector ALUs (the MFMA comparison)
 constexpr int kPrefetchWide = 3;
 
 template <int MODE>
 __host__ __device__ constexpr int threads_for_mode() {
-  return (MODE == kModeTiled || MODE == kModeTiledArgmax) ? kThreadsTiled : kThreads;
+  return (MODE == kModeTiled || MODE == kModeTiledArgmax || MODE == kModeTiledValu) ? kThreadsTiled : kThreads;
 }
 constexpr int waves_for_mode(int mode) {
-  return ((mode == kModeTiled || mode == kModeTiledArgmax) ? kThreadsTiled : kThreads) / 64;
+  return ((mode == kModeTiled || mode == kModeTiledArgmax || mode == kModeTiledValu) ? kThreadsTiled : kThreads) / 64;
 }
 
 // Chained-layer residual update: one workgroup of kChainThreads per
@@ -222,6 +223,30 @@ struct ChainCtl {
 
 hipError_t launch_stream(int N, int mode, const DevMat* mats, const WgRange* ranges, const DevMat& one,
                          int grid, size_t lds_bytes, hipStream_t stream);
+// Single tiled products with few tiles per CU (split_kernel): the first
+// kSplitCounterBytes of a single product's workspace hold one arrival counter
+// per tile (zero between calls: each call leaves them zero, so the workspace
+// must be zero before its first use); every single product's other scratch
+// (tile-chunk parts, chunk partial sums) lies past them.
+constexpr size_t kSplitCounterBytes = 16384;
+constexpr int kSplitMaxTiles = (int)(kSplitCounterBytes / 4);
+// A tile-chunk part: 16 rows x N <= 8 columns of FP32.
+constexpr size_t kSplitPartBytes = 512;
+// Tiles per CU below which a single tiled product splits tiles across waves
+// and workgroups (above it, whole tiles per workgroup balance within 1/8).
+constexpr int kSplitTilesPerCu = 8;
+// Tile-chunk parts one workgroup may write (its LDS list of arrivals), and
+// K chunks at most (the parts a finishing workgroup adds).
+constexpr int kSplitArrivalsMax = 64;
+constexpr int kSplitChunksMax = 24;
+// Threads per workgroup of the split kernel, and steps in flight per lane.
+constexpr int kSplitThreads = 512;
+constexpr int kSplitPrefetch = 3;
+// LDS the split kernel declares statically (its arrival lists), kept free
+// of its dynamic LDS.
+constexpr uint32_t kSplitStaticLds = 1024;
+hipError_t launch_split(int N, const DevMat& one, uint32_t* counters, float* parts, int slots_per_wave, int grid,
+                        size_t lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevMat& one, int grid, int N,
                          hipStream_t stream, const int32_t* n_dev = nullptr);
 // the tiled verify pass with N read from n_dev (a plan prepared for N = 8)

@@ -25,13 +25,17 @@
 //  * The N activation columns of the current K chunk live in LDS, staged
 //    once per (matrix, chunk) by the whole workgroup, laid out so that each
 //    MFMA's A operand is one conflict-free 16-byte read per lane.
-//  * K is split into chunks only to fit LDS (<= 8704 k) or, for a single
-//    small GEMM, to give every wave work.  Partial sums of split tiles go
-//    to a workspace; the last wave to finish a tile (arrival counter) adds
-//    them in chunk order, so results never depend on timing.
+//  * In a verify pass K is split into chunks only to fit LDS (<= 8704 k).
+//    Large split matrices of an all-tiled pass keep their chunk sums in LDS
+//    (blocked splits); others write them to the workspace for reduce_kernel,
+//    which adds them in chunk order.  Results never depend on timing.
 //  * A verify pass is one launch over a table of matrices: the units
 //    (matrix, chunk, 16-row tile) are split into one contiguous run per
-//    workgroup, balanced by bytes on the host.
+//    workgroup, balanced by bytes on the host, with a dynamic tail.
+//  * A single tiled product with few tiles per CU (split_kernel) cuts its
+//    steps into one run per workgroup and one piece per wave; tiles whose K
+//    chunks end in different workgroups are finished by the last one to
+//    arrive (an arrival counter per tile), adding the parts in chunk order.
 //
 // Numerics do not depend on N: a column's A rows, its MFMA sums, its FMA
 // rescale chain and its chunk sum are the same whatever the other columns
@@ -52,6 +56,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(3))) unsigned u32x3;
 
 // Raw buffer resource word 3 for gfx9-family raw (untyped) buffer access.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -188,6 +193,34 @@ __device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0
     u32x4 v[kStageLoads];
     stage_x_load<N>(v, x, K, k0, klen, kc_pad, p0);
     stage_x_store<N>(v, lds, kc_pad, p0);
+  }
+}
+
+// All pieces of one K chunk in flight at once, with direct buffer-to-LDS
+// loads (the tiled verify-pass kernels): instruction j of wave w writes the
+// 64 consecutive pieces q = j * blockDim.x + 64 w + lane of the LDS order
+// (q = kc * N + n at byte 16 q; a buffer-to-LDS load puts lane l's 16 bytes
+// at its base plus 16 l).  Pieces past the chunk's last k read past the
+// end of X, which the range check returns as zeros.  No registers hold X on
+// the way, so a chunk of any size is one round trip, where staging through
+// registers (eight 16-byte loads per thread per round) took two or three
+// at N = 8.  The caller waits for the loads and synchronizes.
+template <int N>
+__device__ __forceinline__ void stage_x_direct(char* lds, const uint16_t* __restrict__ x, int K, int k0, int klen,
+                                               int kc_pad) {
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc_uniform(x, (uint64_t)N * (uint64_t)K * 2u);
+  const int valid = klen / 8;
+  const int total = kc_pad * N;
+  const int lane = (int)(threadIdx.x & 63);
+  const int wbase = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63u));
+  for (int q0 = wbase; q0 < total; q0 += (int)blockDim.x) {
+    const int q = q0 + lane;
+    const int kc = q / N, n = q - kc * N;
+    // (N K 2 < 2^31: an offset of 2^31 is past every X)
+    const uint32_t off = kc < valid ? (uint32_t)((n * K + k0 + 8 * kc) * 2) : 0x80000000u;
+    if (q < total)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(lds + (size_t)q0 * 16), 16,
+                                               off, 0, 0, 0);
   }
 }
 
@@ -489,9 +522,22 @@ constexpr int kEpiGlu = 2;
 // block's tiles wait in LDS (one 512-byte slot per tile of the block, placed
 // as part_a_slots says) for the next chunk, which adds its own to them, in
 // chunk order as reduce_kernel does, and the last chunk stores y.
-template <int N, int PF, bool FP8, int EPI, bool BLK, typename Pre, typename Stage>
+//
+// VALU (NVFP4 only): the step on the vector ALUs instead of the matrix cores,
+// the other side of the MFMA/VALU comparison.  Lane l = c + 16 g holds, for
+// half h and MFMA step j, the eight codes of row c at k = 128 h + 32 j + 8 g
+// + 0..7 of its step (one 16-k scale block, whose scale is the lane's byte
+// j); it widens them to BF16 (exact), forms for every column n the eight
+// products with X by four BF16 dot-2 instructions (FP32 sums), and adds them,
+// times the block scale, to its FP32 sum for column n.  At a tile's end the
+// four lanes of row c (g = 0..3) add their sums (a fixed butterfly) and the
+// results are laid out as the MFMA epilogue expects them (lanes 0..31: rows
+// n = 4 (lane / 16) + r of m = lane % 16; lanes 32..63: zero), so the same
+// epilogue follows.
+template <int N, int PF, bool FP8, int EPI, bool BLK, bool VALU = false, typename Pre, typename Stage>
 __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t end, int64_t ubase, int ptile0,
                           char* lds, uint64_t* bestk, Pre&& pre, Stage&& stage) {
+  static_assert(!(VALU && FP8), "the vector-ALU step is the NVFP4 one");
   pre();
   if (first >= end) {
     stage();
@@ -568,6 +614,29 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(stv[t], part[t][r], acc[r]);
   };
+  // NVFP4 on the vector ALUs: half h of the step cs
+  float accv[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) accv[n] = 0.f;
+  auto half_valu = [&](const u32x4& e, uint32_t sb, int h, int cs) {
+    const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
+    const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, true);
+    const float stv[4] = {s01.x, s01.y, s23.x, s23.y};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 w = e2m1x8_to_bf16(e[j]);
+      const uint32_t xb = (uint32_t)((32 * cs + 16 * h + 4 * j + g) * N) * 16u;
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const bf16x8 xv = lds_read16(lds, xb + 16u * n);
+        float d = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[0], w[1]}, bf16x2{xv[0], xv[1]}, 0.f, false);
+        d = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[2], w[3]}, bf16x2{xv[2], xv[3]}, d, false);
+        d = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[4], w[5]}, bf16x2{xv[4], xv[5]}, d, false);
+        d = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[6], w[7]}, bf16x2{xv[6], xv[7]}, d, false);
+        accv[n] = __builtin_fmaf(stv[j], d, accv[n]);
+      }
+    }
+  };
   // FP8: one 64-k segment (16 bytes of the lane's row)
   auto segment = [&](const u32x4& d, uint32_t xo) {
     bf16x8 a[2], b[2];
@@ -616,11 +685,34 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
     if constexpr (FP8) {
       segment(c0[slot], xo);
       segment(c1[slot], xo + 128u * N);
+    } else if constexpr (VALU) {
+      half_valu(c0[slot], sw[slot].x, 0, cst);
+      half_valu(c1[slot], sw[slot].y, 1, cst);
     } else {
       half(c0[slot], sw[slot].x, xo);
       half(c1[slot], sw[slot].y, xo + 256u * N);
     }
     const bool fin = cst == nst - 1;
+    if constexpr (VALU) {
+      if (fin) {
+        // the four k groups of row c, then the MFMA epilogue's layout
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          accv[n] += __shfl_xor(accv[n], 16);
+          accv[n] += __shfl_xor(accv[n], 32);
+        }
+        const int nb = (lane & 16) ? 4 : 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = 0.f;
+#pragma unroll
+          for (int n = 0; n < N; ++n) v = (n == nb + r) ? accv[n] : v;
+          acc[r] = lane < 32 ? v : 0.f;
+        }
+#pragma unroll
+        for (int n = 0; n < N; ++n) accv[n] = 0.f;
+      }
+    }
     if (fin && EPI == kEpiGlu) {
       // sums sit at lane 16 * (n / 4) + c (and again 32 lanes up); the gate
       // row c < 8 and the up row c + 8 of one f are 8 lanes apart
@@ -734,6 +826,312 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
 #pragma unroll
   for (int i = 0; i < PF; ++i)
     if (q0 + i < Q) compute_next(i);
+}
+
+// ---- single products with few tiles per CU: tiles split across waves --------
+// A product of T tiles x S steps is cut into C short K chunks ("tile-chunks"
+// of s steps; chunk-major order: every tile's chunk 0, then chunk 1, ...).
+// Each workgroup takes a run of whole tile-chunks of about U / G steps and
+// splits the run's steps into one equal piece per wave, so that every CU
+// streams about the same bytes with all its waves from the start, however
+// few tiles there are.  A wave streams its piece as one sequence (a tile's
+// steps of one chunk are contiguous in the tiled layout, the next tile's
+// follow) and leaves the sums of each tile-chunk it touched in an LDS slot;
+// the workgroup adds, per tile-chunk, its waves' slots in wave order (k
+// order).  With one chunk the tile is stored as y; otherwise the tile-chunk
+// sum is a part in the workspace, and the workgroup whose part is the C-th
+// to arrive at the tile (an arrival counter per tile) adds the C parts in
+// chunk order and stores y.  The cut depends on (M, K) and the grid only, so
+// column n has the same bits for every N.
+
+// s_waitcnt that waits only for the vector-memory count to reach V (the
+// gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 at
+// their maximum, i.e. not waited for).
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+}
+
+// Steps [e0, e1) of chunk `chunk` (chunk-local index e = tile * nst + step)
+// streamed by this wave; the sums of the j-th tile it touches go to LDS at
+// slots + 512 j (lanes 0..31: four floats, rows n = 4 (lane / 16) + r of
+// output m = 16 tile + lane % 16).  X of the chunk was requested before this
+// call; once the wave's first PF steps of weight loads are in flight, it
+// waits for X alone (loads complete in order) and synchronizes the workgroup.
+template <int N, bool FP8>
+__device__ void split_piece(const DevMat& mt, int chunk, int nst, int e0, int e1, const char* lds, char* slots) {
+  constexpr int PF = kSplitPrefetch;
+  constexpr int kStep = FP8 ? kFp8TileStepK : kTileStepK;
+  constexpr uint32_t kBlock = FP8 ? kFp8TileBlockBytes : kTileBlockBytes;
+  constexpr int kLoads = FP8 ? 2 : 3;  // vector-memory loads per step
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int cnt = e1 - e0;
+  if (cnt <= 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    return;
+  }
+  const uint32_t steps_per_row = (uint32_t)((mt.K + kStep - 1) / kStep);
+  const uint32_t base_step = (uint32_t)(chunk * (mt.kc / kStep));
+  const uint64_t total = (uint64_t)mt.ntiles * steps_per_row * kBlock;  // < 2^32 (checked on the host)
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc_uniform(mt.w, total);
+  const uint32_t vc = 16u * lane;
+  const uint32_t vs = (uint32_t)kTileCodeBytes + 8u * (uint32_t)(((lane >> 5) << 4) + c);
+  bool active;
+  uint32_t xoff, xstep;
+  if constexpr (FP8) {
+    active = c < N;
+    xoff = active ? (uint32_t)((2 * g * N + c) * 16) : kZeroOffset<N>();
+    xstep = active ? 256u * N : 0u;
+  } else {
+    active = ((c >> 3) == (g >> 1)) && ((c & 7) < N);
+    xoff = active ? (uint32_t)((g * N + (c & 7)) * 16) : kZeroOffset<N>();
+    xstep = active ? 512u * N : 0u;
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  u32x4 c0[PF], c1[PF];
+  u32x2 sw[PF];
+  const int t_first = e0 / nst;
+  // next step to load (past the end: the last one again)
+  int lt = t_first, ls = e0 - t_first * nst, ln = 0;
+  auto load_next = [&](int slot) {
+    const uint32_t b = ((uint32_t)lt * steps_per_row + base_step + (uint32_t)ls) * kBlock;
+    c0[slot] = bload16t(rw, b + vc);
+    c1[slot] = bload16t(rw, b + 1024u + vc);
+    if constexpr (!FP8) sw[slot] = bload8t(rw, b + vs);
+    if (ln < cnt) {
+      ++ln;
+      if (ln < cnt && ++ls == nst) { ls = 0; ++lt; }
+    }
+  };
+  auto half = [&](const u32x4& e, uint32_t sb, uint32_t xo) {
+    const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
+    const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(sb, true);
+    const float stv[4] = {s01.x, s01.y, s23.x, s23.y};
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = lds_read16(lds, xo + t * 64u * N);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b[t] = e2m1x8_to_bf16(e[t]);
+    f32x4 part[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      part[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t], b[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(stv[t], part[t][r], acc[r]);
+  };
+  auto segment = [&](const u32x4& d, uint32_t xo) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) a[u] = lds_read16(lds, xo + u * 16u * N);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) b[u] = e4m3x8_to_bf16(d[2 * u], d[2 * u + 1]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+  };
+  // next step to compute
+  int ct = t_first, cs = e0 - t_first * nst, cn = 0;
+  auto compute_next = [&](int slot) {
+    const uint32_t xo = xoff + (uint32_t)cs * xstep;
+    if constexpr (FP8) {
+      segment(c0[slot], xo);
+      segment(c1[slot], xo + 128u * N);
+    } else {
+      half(c0[slot], sw[slot].x, xo);
+      half(c1[slot], sw[slot].y, xo + 256u * N);
+    }
+    ++cn;
+    if (cs == nst - 1 || cn == cnt) {
+      // the swap gives every lane the low half's value (.x) and the high
+      // half's (.y): NVFP4 blocks 0 and 1 of one (n, m), added in that
+      // order; FP8 rows n < 8 (the high half is zero)
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const u32x2 p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
+        o[r] = FP8 ? __uint_as_float(p.x) : __uint_as_float(p.x) + __uint_as_float(p.y);
+        acc[r] = 0.f;
+      }
+      if (lane < 32) *reinterpret_cast<f32x4*>(slots + 512 * (ct - t_first) + 16 * lane) = o;
+    }
+    if (++cs == nst) { cs = 0; ++ct; }
+  };
+#pragma unroll
+  for (int i = 0; i < PF; ++i) load_next(i);
+  wait_vmcnt<PF * kLoads>();
+  __syncthreads();
+  int q0 = 0;
+  for (; q0 + PF <= cnt; q0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      compute_next(i);
+      load_next(i);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (q0 + i < cnt) compute_next(i);
+}
+
+// Tile-chunk parts in the workspace: part (chunk, tile) holds 16 rows x N
+// columns, float (m, n) at word m N + n; lane l < 32 of a workgroup's sums
+// holds columns n = 4 (l / 16) + r of row m = l % 16.
+template <int N>
+__device__ __forceinline__ void store_part(const f32x4& v, __amdgpu_buffer_rsrc_t r, uint32_t base, int lane) {
+  const int h = lane >> 4, m = lane & 15;
+  const int cnt = N - 4 * h;  // columns this lane holds (lanes 0..31 only)
+  const uint32_t off = base + (uint32_t)(m * N + 4 * h) * 4u;
+  if (lane >= 32 || cnt <= 0) return;
+  // written through to memory (device scope): a completed store is what
+  // another workgroup's device-scope load returns
+  if (cnt >= 4) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kAuxOut);
+  else if (cnt == 3)
+    __builtin_amdgcn_raw_buffer_store_b96(u32x3{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2])},
+                                          r, (int)off, 0, kAuxOut);
+  else if (cnt == 2) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{v[0], v[1]}), r, (int)off, 0, kAuxOut);
+  else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, (int)off, 0, kAuxOut);
+}
+template <int N>
+__device__ __forceinline__ f32x4 load_part(__amdgpu_buffer_rsrc_t r, uint32_t base, int lane) {
+  const int h = (lane >> 4) & 1, m = lane & 15;
+  const int cnt = N - 4 * h;
+  const uint32_t off = base + (uint32_t)(m * N + 4 * h) * 4u;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (cnt >= 4) v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAuxOut));
+  else if (cnt == 3) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b96(r, (int)off, 0, kAuxOut);
+    v = f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), 0.f};
+  } else if (cnt == 2) {
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kAuxOut));
+    v = f32x4{__uint_as_float(w[0]), __uint_as_float(w[1]), 0.f, 0.f};
+  } else if (cnt == 1) {
+    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kAuxOut));
+  }
+  return v;
+}
+
+template <int N, bool FP8>
+__global__ __launch_bounds__(kSplitThreads) void split_kernel(DevMat mt, uint32_t* __restrict__ counters,
+                                                              float* __restrict__ parts, int slots_per_wave) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int kW = kSplitThreads / 64;
+  constexpr int kStep = FP8 ? kFp8TileStepK : kTileStepK;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int S = (mt.K + kStep - 1) / kStep;
+  const int T = mt.ntiles, C = mt.nchunks;
+  const int s_full = mt.kc / kStep, s_last = S - (C - 1) * s_full;
+  // The run: workgroups [G c / C, G (c + 1) / C) take chunk c, each an
+  // equal share of its tiles [ta, tb) (whole tile-chunks), so that a run
+  // never leaves its chunk and X is staged once.
+  const int G = gridDim.x, g = blockIdx.x;
+  const int ch = (C * (g + 1) - 1) / G;
+  const int g0 = G * ch / C, gc = G * (ch + 1) / C - g0;
+  const int ta = T * (g - g0) / gc, tb = T * (g - g0 + 1) / gc;
+  const int la = ta * (ch == C - 1 ? s_last : s_full), lb = tb * (ch == C - 1 ? s_last : s_full);
+  char* const slots = lds + kPartOffset<N>();
+  char* const my_slots = slots + (size_t)wave * slots_per_wave * 512;
+  __shared__ int s_arrive[kSplitArrivalsMax];  // tile-chunks (c T + t) this workgroup wrote parts of
+  __shared__ int s_tile0[kSplitThreads / 64], s_tile1[kSplitThreads / 64];
+  __shared__ int s_narrive;
+  if (threadIdx.x == 0) s_narrive = 0;
+  for (int i = threadIdx.x; i < kZeroBytes<N>() / 16; i += blockDim.x)
+    *reinterpret_cast<u32x4*>(lds + kZeroOffset<N>() + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc_uniform(mt.rs, FP8 ? (uint64_t)mt.M * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc_uniform(mt.y, (uint64_t)N * mt.M * 4u);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc_uniform(parts, (uint64_t)C * T * kSplitPartBytes);
+  auto store_y = [&](int t, const f32x4& v) {
+    const int m = 16 * t + (lane & 15);
+    // the output scale of lane l's row m = 16 t + l % 16 (rows past M read 0)
+    const float sc = FP8 ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, (int)(m * 4), 0, 0)) : mt.g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = 4 * (lane >> 4) + r;
+      if (lane < 32 && n < N && m < mt.M) bstore4(sc * v[r], ro, (uint32_t)((n * mt.M + m) * 4));
+    }
+  };
+
+  if (ta < tb) {
+    const int nst = ch == C - 1 ? s_last : s_full;
+    const int k0 = ch * mt.kc;
+    const int klen = min(mt.kc, mt.K - k0);
+    // this chunk of X is requested before the pieces' first weight loads;
+    // split_piece waits for it
+    stage_x_direct<N>(lds, mt.x, mt.K, k0, klen, nst * (kStep / 8));
+    __builtin_amdgcn_sched_barrier(0);
+    const int e0 = la + (lb - la) * wave / kW, e1 = la + (lb - la) * (wave + 1) / kW;
+    // each wave's first and last tile, for the sums below
+    if (lane == 0) {
+      s_tile0[wave] = e0 / nst;
+      s_tile1[wave] = e0 < e1 ? (e1 - 1) / nst : -1;
+    }
+    split_piece<N, FP8>(mt, ch, nst, e0, e1, lds, my_slots);
+    __syncthreads();
+    // per tile of the run: the sums of the waves that touched it, in wave
+    // order (every wave's slot read issued before the additions)
+    const int my_t0 = s_tile0[lane & (kW - 1)], my_t1 = s_tile1[lane & (kW - 1)];
+    for (int t = ta + wave; t < tb; t += kW) {
+      f32x4 v[kW];
+      bool use[kW];
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const int t0 = __shfl(my_t0, w), t1 = __shfl(my_t1, w);
+        use[w] = t >= t0 && t <= t1;
+        const int j = use[w] ? t - t0 : 0;
+        v[w] = *reinterpret_cast<const f32x4*>(slots + ((size_t)w * slots_per_wave + j) * 512 + 16 * (lane & 31));
+      }
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kW; ++w)
+        if (use[w])
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum[r] += v[w][r];
+      if (C == 1) {
+        store_y(t, sum);
+      } else {
+        store_part<N>(sum, rp, (uint32_t)(ch * T + t) * kSplitPartBytes, lane);
+        if (lane == 0) {
+          const int i = atomicAdd(&s_narrive, 1);
+          if (i < kSplitArrivalsMax) s_arrive[i] = ch * T + t;  // (the host keeps i below the bound)
+        }
+      }
+    }
+  }
+  // arrivals, once every wave's part stores have completed (written
+  // through, so visible device-wide): one per part, all at once
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int narrive = min(s_narrive, kSplitArrivalsMax);
+  if (narrive == 0) return;
+  __shared__ int s_done[kSplitArrivalsMax];  // the tile, if this part completed it, else -1
+  if ((int)threadIdx.x < narrive) {
+    const int t = s_arrive[threadIdx.x] % T;
+    const uint32_t old = __hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_done[threadIdx.x] = (int)old + 1 == C ? t : -1;
+  }
+  __syncthreads();
+  // the tiles this workgroup completes: the C parts in chunk order
+  for (int i = wave; i < narrive; i += kW) {
+    const int t = s_done[i];
+    if (t < 0) continue;
+    // (every part's load in flight at once, then added in chunk order)
+    f32x4 v[kSplitChunksMax];
+#pragma unroll
+    for (int j = 0; j < kSplitChunksMax; ++j)
+      if (j < C) v[j] = load_part<N>(rp, (uint32_t)(j * T + t) * kSplitPartBytes, lane);
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kSplitChunksMax; ++j)
+      if (j < C)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sum[r] += v[j][r];
+    store_y(t, sum);
+    if (lane == 0) __hip_atomic_store(&counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---- one FP8-row unit ------------------------------------------------------
@@ -890,7 +1288,7 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
   // the dynamic tail until none is left
   // (only the tiled kernel has the claim loop: plans of other kernels have no
   // tail, and the loop's presence alone slowed the plain-layout kernels)
-  DynSched* const dyn = (MODE == kModeTiled && mats)
+  DynSched* const dyn = ((MODE == kModeTiled || MODE == kModeTiledValu) && mats)
                             ? reinterpret_cast<DynSched*>(const_cast<WgRange*>(ranges) + gridDim.x + 1)
                             : nullptr;
   __shared__ uint32_t s_claim;
@@ -967,6 +1365,9 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       sync_first();
       if constexpr (kEarlyX) {
         stage_x_rest<N>(xpre, lds, mt.x, mt.K, k0, klen, kc_pad);
+      } else if constexpr (MODE == kModeTiled || MODE == kModeTiledArgmax || MODE == kModeTiledValu) {
+        stage_x_direct<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (and every older one) are done
       } else {
         stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
       }
@@ -983,6 +1384,13 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       else
         tiled_run<N, kPrefetchTiled, false, kEpiStore, true>(mt, chunk, share0, share1, ubase, ptile0, lds, bestk, pre,
                                                               stage);
+    } else if constexpr (MODE == kModeTiledValu) {
+      if (mt.fmt == kFmtFp8RowTiled)
+        tiled_run<N, kPrefetchTiled, true, kEpiStore, true>(mt, chunk, share0, share1, ubase, ptile0, lds, bestk, pre,
+                                                             stage);
+      else
+        tiled_run<N, kPrefetchTiled, false, kEpiStore, true, true>(mt, chunk, share0, share1, ubase, ptile0, lds,
+                                                                    bestk, pre, stage);
     } else if constexpr (MODE == kModeTiledArgmax) {
       if (mt.fmt == kFmtFp8RowTiled)
         tiled_run<N, kPrefetchTiled, true, kEpiArgmax, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, pre,
@@ -1275,13 +1683,13 @@ hipError_t launch_reduce(const DevMat* mats, const ReduceTask* tasks, const DevM
 
 // The dynamic-LDS limit of a kernel is raised once per device (the
 // attribute is per device; a bit per device ordinal, set after success).
-static hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done) {
+static hipError_t allow_lds(const void* fn, std::atomic<uint64_t>& done, uint32_t max_bytes = kMaxLdsBytes) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
   if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
-  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_bytes);
   if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
   return e;
 }
@@ -1394,6 +1802,41 @@ hipError_t launch_accept(const uint64_t* keys, int groups, int N, const int32_t*
 }
 
 // ---- host-side launchers ---------------------------------------------------
+template <int N, bool FP8>
+static hipError_t launch_split_nf(const DevMat& one, uint32_t* counters, float* parts, int slots_per_wave, int grid,
+                                  size_t lds_bytes, hipStream_t stream) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_lds(reinterpret_cast<const void*>(&split_kernel<N, FP8>), lds_set, 160u * 1024u - kSplitStaticLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((split_kernel<N, FP8>), dim3(grid), dim3(kSplitThreads), lds_bytes, stream, one, counters,
+                     parts, slots_per_wave);
+  return hipGetLastError();
+}
+
+template <int N>
+static hipError_t launch_split_n(const DevMat& one, uint32_t* counters, float* parts, int slots_per_wave, int grid,
+                                 size_t lds_bytes, hipStream_t stream) {
+  return one.fmt == kFmtFp8RowTiled
+             ? launch_split_nf<N, true>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream)
+             : launch_split_nf<N, false>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+}
+
+hipError_t launch_split(int N, const DevMat& one, uint32_t* counters, float* parts, int slots_per_wave, int grid,
+                        size_t lds_bytes, hipStream_t stream) {
+  switch (N) {
+    case 1: return launch_split_n<1>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    case 2: return launch_split_n<2>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    case 3: return launch_split_n<3>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    case 4: return launch_split_n<4>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    case 5: return launch_split_n<5>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    case 6: return launch_split_n<6>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    case 7: return launch_split_n<7>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    case 8: return launch_split_n<8>(one, counters, parts, slots_per_wave, grid, lds_bytes, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int N, int MODE>
 static hipError_t launch_nm(const DevMat* mats, const WgRange* ranges, const DevMat& one, int grid,
                             size_t lds_bytes, hipStream_t stream) {
@@ -1417,6 +1860,7 @@ static hipError_t launch_n(int mode, const DevMat* mats, const WgRange* ranges, 
     case kModeTiledArgmax: return launch_nm<N, kModeTiledArgmax>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeTiledGlu: return launch_nm<N, kModeTiledGlu>(mats, ranges, one, grid, lds_bytes, stream);
     case kModeTiledWide: return launch_nm<N, kModeTiledWide>(mats, ranges, one, grid, lds_bytes, stream);
+    case kModeTiledValu: return launch_nm<N, kModeTiledValu>(mats, ranges, one, grid, lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }

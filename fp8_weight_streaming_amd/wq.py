@@ -132,6 +132,8 @@ _lib.wq_quantize_fp8row.restype = _I
 _lib.wq_quantize_fp8row.argtypes = [_P, _I, _I, _P, _P, _P]
 _lib.wq_quantize_nvfp4.restype = _I
 _lib.wq_quantize_nvfp4.argtypes = [_P, _I, _I, ctypes.c_float, _P, _P, _P]
+_lib.wq_verify_launch_valu.restype = _I
+_lib.wq_verify_launch_valu.argtypes = [ctypes.POINTER(WqVerifyPlan), _P]
 _lib.wq_verify_launch_n.restype = _I
 _lib.wq_verify_launch_n.argtypes = [ctypes.POINTER(WqVerifyPlan), _P, _P]
 _lib.wq_gemm_fp8row_tiled.restype = _I
@@ -154,7 +156,7 @@ EXPORTED = ["wq_nvfp4_tiled_bytes", "wq_nvfp4_tile", "wq_nvfp4_untile", "wq_gemm
             "wq_gemm_nvfp4_tiled_noalloc", "wq_status_string", "wq_gemm_workspace_bytes", "wq_gemm_split", "wq_gemm_nvfp4", "wq_gemm_fp8row",
             "wq_fp8_tiled_bytes", "wq_fp8_tile", "wq_fp8_untile", "wq_gemm_fp8row_tiled",
             "wq_head_accept_workspace_bytes", "wq_head_accept", "wq_quantize_fp8row", "wq_quantize_nvfp4",
-            "wq_verify_launch_n", "wq_nvfp4_tile_glu", "wq_mlp_chain_workspace_bytes", "wq_mlp_chain_split",
+            "wq_verify_launch_n", "wq_verify_launch_valu", "wq_nvfp4_tile_glu", "wq_mlp_chain_workspace_bytes", "wq_mlp_chain_split",
             "wq_mlp_chain_prepare", "wq_mlp_chain_launch", "wq_mlp_chain_launch_persistent",
             "wq_verify_workspace_bytes", "wq_verify_pass", "wq_verify_prepare", "wq_verify_launch",
             "wq_probe_sink_words", "wq_probe_read", "wq_probe_copy", "wq_probe_read_write_bytes",
@@ -432,6 +434,12 @@ def wq_quantize_nvfp4(w, global_scale: float, codes, scales, stream=None, M: Opt
         K = w.shape[1]
     _check(_lib.wq_quantize_nvfp4(_ptr(w), M, K, float(global_scale), _ptr(codes), _ptr(scales), _stream(stream)),
            "wq_quantize_nvfp4")
+
+
+def wq_verify_launch_valu(plan: WqVerifyPlan, stream=None):
+    """Launch a prepared tiled pass with its NVFP4 steps on the vector ALUs
+    (the matrix-core comparison)."""
+    _check(_lib.wq_verify_launch_valu(ctypes.byref(plan), _stream(stream)), "wq_verify_launch_valu")
 
 
 def wq_verify_launch_n(plan: WqVerifyPlan, n_device, stream=None):

@@ -29,13 +29,18 @@
  *    1-8 columns "with column invariance"; the crit README's "Kernel
  *    workbench" asks for the same bits on a repeat).  How K is split
  *    depends only on (M, K) and the device, never on N.
- *  - Workspace: some shapes split K across workgroups and need scratch
- *    memory for the chunks' partial sums (added in chunk order by a second,
- *    small kernel on the same stream).  Query its size with the matching
- *    *_workspace_bytes call; pass a device buffer at least that large
- *    (16-byte aligned), or NULL/0 when the query returns 0.  Its contents
- *    need no initialization and are scratch after the call.  Calls that
- *    share one workspace must not overlap in time (same stream is fine).
+ *  - Workspace: some shapes split their work across workgroups and need
+ *    scratch memory.  Query its size with the matching *_workspace_bytes
+ *    call; pass a device buffer at least that large (16-byte aligned), or
+ *    NULL/0 when the query returns 0.  Single-matrix calls (wq_gemm_*): the
+ *    buffer must be all zero before its first use (torch.zeros, hipMemset);
+ *    its first 16 KiB hold arrival counters that every call leaves zero
+ *    again, and the rest is scratch, so any later single-matrix call may
+ *    reuse it without clearing (a buffer used by wq_verify_pass or anything
+ *    else in between must be zeroed again).  wq_verify_pass's workspace
+ *    needs no initialization (its prepare call writes what it needs).
+ *    Calls that share one workspace must not overlap in time (same stream
+ *    is fine).
  *  - Threading: the library keeps no state besides a per-device cache of
  *    the compute-unit count; calls are reentrant on different streams with
  *    different workspaces.
@@ -75,12 +80,19 @@ const char* wq_status_string(wq_status s);
 size_t wq_gemm_workspace_bytes(int fmt, int M, int K, int N);
 
 /* The K split a call will use: K is cut into *n_chunks chunks of *k_chunk
- * (the last may be shorter).  in_verify_pass = 0 asks about
- * wq_gemm_nvfp4 / wq_gemm_fp8row on the current device, 1 about a matrix
+ * (the last may be shorter).  in_verify_pass = 0 asks about the
+ * single-matrix calls (wq_gemm_*) on the current device, 1 about a matrix
  * inside wq_verify_pass, 2 about a matrix that wq_verify_pass computes in
  * blocks (a large split matrix of a pass of tiled matrices only; see
  * wq_verify_pass).  Two calls that report the same split compute
- * bit-identical results for the same matrix and columns. */
+ * bit-identical results for the same matrix and columns.
+ * *k_chunk = 0 (single calls on the tiled formats with fewer than 8 row
+ * tiles of 16 per compute unit) reports the split-tile mode: the steps of
+ * the *n_chunks K chunks are cut into one equal run per workgroup and one
+ * equal piece per wave, each tile's pieces are added in k order (in LDS,
+ * then across workgroups by the last one to arrive), so every compute unit
+ * streams the same bytes; the cut depends on (M, K) and the device, never on
+ * N, and the rounding differs from that of the chunked calls. */
 wq_status wq_gemm_split(int fmt, int M, int K, int in_verify_pass, int* k_chunk, int* n_chunks);
 
 /* NVFP4 weights.
@@ -263,6 +275,19 @@ wq_status wq_verify_launch(const wq_verify_plan* plan, void* stream);
  * x[0..n-1] . W^T, bit for bit what a plan prepared for N = n computes;
  * rows n..7 of y are left untouched.  Launch only (capture-safe). */
 wq_status wq_verify_launch_n(const wq_verify_plan* plan, const int32_t* n_device, void* stream);
+
+/* The same prepared pass with every NVFP4 step computed on the vector ALUs
+ * (BF16 dot-2 instructions, FP32 sums) instead of the matrix cores; tiled
+ * FP8-row matrices of the plan keep the matrix-core step.  It exists to
+ * price that choice: at these column counts the product streams weights,
+ * and the matrix cores are used only because they are measured faster
+ * (the crit-hub engine card, section "Design", row "GEMVs", reads the
+ * weights into tensor-core fragments on its GPU).  `plan` must come from
+ * wq_verify_prepare over tiled matrices only.  Results agree with
+ * wq_verify_launch within the products' tolerance (not bit for bit: the
+ * sums are grouped differently); column n still has the same bits for every
+ * N.  Launch only. */
+wq_status wq_verify_launch_valu(const wq_verify_plan* plan, void* stream);
 
 /* Greedy draft acceptance fused onto the output-head product (the crit
  * README, section "Core": greedy draft acceptance is part of sampling;

@@ -164,8 +164,84 @@ static wq_matrix mk(int fmt, int M, int K) {
   return d;
 }
 
+// The single-product split plan (tile_split_plan) replayed as split_kernel
+// walks it: workgroups shared out among the chunks, each an equal share of
+// its chunk's tiles, wave pieces, the tiles each piece touches (its LDS
+// slots), the parts each workgroup writes and the arrivals per tile.
+// Checks: every (tile, step) once; slots and arrivals within their bounds;
+// the launch's LDS at N = 8 within the limit; with several chunks, every
+// tile-chunk's part written once (C arrivals per tile), with one chunk, none.
+static int check_tile_split(int fmt, int M, int K, int cus) {
+  const TileSplit ts = tile_split_plan(fmt, M, K, cus);
+  if (!ts.ok) return 0;
+  const int sk = seg_k(fmt);
+  const int64_t T = ceil_div(M, 16), S = ceil_div(K, sk);
+  const int64_t C = ts.chunks.nchunks;
+  const int64_t sf = ts.chunks.kc / sk, sl = S - (C - 1) * sf;
+  const int64_t U = T * S, G = ts.grid;
+  const int W = kSplitThreads / 64;
+  int bad = 0;
+  if (ts.chunks.ntiles != T || sl < 1 || sl > sf || C > kSplitChunksMax) ++bad;
+  if (lds_bytes_for(8) + (uint64_t)W * ts.slots * kSplitPartBytes + kSplitStaticLds > 160u * 1024u) ++bad;
+  if (G < C || G > cus || T > kSplitMaxTiles || U >= (1ll << 31)) ++bad;
+  std::vector<int> seen(U, 0), parts((size_t)(C * T), 0);
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t ch = (C * (g + 1) - 1) / G;
+    const int64_t g0 = G * ch / C, gc = G * (ch + 1) / C - g0;
+    if (g < g0 || g >= g0 + gc || ch >= C) { ++bad; continue; }
+    const int64_t ta = T * (g - g0) / gc, tb = T * (g - g0 + 1) / gc;
+    if (ta >= tb) continue;
+    const int64_t n = ch == C - 1 ? sl : sf;
+    const int64_t la = ta * n, lb = tb * n;
+    for (int w = 0; w < W; ++w) {
+      const int64_t e0 = la + (lb - la) * w / W, e1 = la + (lb - la) * (w + 1) / W;
+      if (e0 < e1 && (e1 - 1) / n - e0 / n + 1 > ts.slots) ++bad;
+      for (int64_t e = e0; e < e1; ++e) seen[(e / n) * S + ch * sf + e % n] += 1;
+    }
+    if (C > 1) {
+      if (tb - ta > kSplitArrivalsMax) ++bad;
+      for (int64_t t = ta; t < tb; ++t) parts[ch * T + t] += 1;
+    }
+  }
+  for (int64_t i = 0; i < U; ++i)
+    if (seen[i] != 1) { ++bad; break; }
+  for (int64_t i = 0; i < C * T; ++i)
+    if (parts[i] != (C > 1 ? 1 : 0)) { ++bad; break; }
+  if (bad) printf("tile split fmt=%d M=%d K=%d cus=%d: %d problems\n", fmt, M, K, cus, bad);
+  return bad;
+}
+
 int main() {
   int bad = 0;
+  {
+    // the single products of the benchmark, and random small ones
+    int nsplit = 0;
+    const int shapes[][3] = {{kFmtNvfp4Tiled, 1024, 1024}, {kFmtNvfp4Tiled, 17408, 5120},
+                             {kFmtNvfp4Tiled, 5120, 17408}, {kFmtNvfp4Tiled, 1, 32},
+                             {kFmtNvfp4Tiled, 96, 17408},   {kFmtFp8RowTiled, 40, 17424},
+                             {kFmtNvfp4Tiled, 1000, 8736},  {kFmtFp8RowTiled, 1, 16}};
+    for (const auto& sh : shapes)
+      for (int cus : {256, 304, 80, 1}) {
+        bad += check_tile_split(sh[0], sh[1], sh[2], cus);
+        nsplit += tile_split_plan(sh[0], sh[1], sh[2], cus).ok;
+      }
+    std::mt19937 rng(7);
+    for (int it = 0; it < 3000; ++it) {
+      const bool fp8 = rng() % 3 == 0;
+      int K = (fp8 ? 16 : 32) * (1 + (int)(rng() % 1100));
+      const int M = 1 + (int)(rng() % 33000);
+      const int cus = (int[]){1, 3, 64, 256, 304}[rng() % 5];
+      bad += check_tile_split(fp8 ? kFmtFp8RowTiled : kFmtNvfp4Tiled, M, K, cus);
+      nsplit += tile_split_plan(fp8 ? kFmtFp8RowTiled : kFmtNvfp4Tiled, M, K, cus).ok;
+    }
+    const TileSplit c1 = tile_split_plan(kFmtNvfp4Tiled, 17408, 5120, 256);
+    const TileSplit c2 = tile_split_plan(kFmtNvfp4Tiled, 5120, 17408, 256);
+    printf("tile split: %d plans checked; 17408x5120: ok=%d grid=%d chunks=%d kc=%d slots=%d; "
+           "5120x17408: ok=%d grid=%d chunks=%d kc=%d slots=%d\n",
+           nsplit, c1.ok, c1.grid, c1.chunks.nchunks, c1.chunks.kc, c1.slots, c2.ok, c2.grid, c2.chunks.nchunks,
+           c2.chunks.kc, c2.slots);
+    if (!c1.ok || !c2.ok) ++bad;
+  }
   std::vector<wq_matrix> dense;
   for (int l = 0; l < 64; ++l) {
     dense.push_back(mk(kFmtNvfp4Tiled, 7168, 5120));

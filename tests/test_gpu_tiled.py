@@ -333,6 +333,16 @@ def test_blocked_split_pass(wq):
             for m, (rows, yr, ar) in zip(mats, refs):
                 assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "N=%d launch %d M=%d K=%d" % (N, launch, m.M, m.K))
         outs[N] = [m.y.cpu().numpy() for m in mats]
+        if N == 8:
+            # the same plan with the NVFP4 steps on the vector ALUs (blocked
+            # epilogue included)
+            for m in mats:
+                m.y.fill_(float("nan"))
+            print("blocked pass N=8, vector-ALU steps", flush=True)
+            wq.wq_verify_launch_valu(plan)
+            torch.cuda.synchronize()
+            for m, (rows, yr, ar) in zip(mats, refs):
+                assert_close(m.y.cpu().numpy()[:, rows], yr, ar, "valu N=8 M=%d K=%d" % (m.M, m.K))
     for i, (_, d) in enumerate(host):
         for N in (1, 3, 5):
             assert np.array_equal(outs[N][i].view(np.uint32), outs[8][i][:N].view(np.uint32)), "M=%d: N=%d differs" % (d.M, N)

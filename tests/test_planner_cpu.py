@@ -1,8 +1,10 @@
-"""The verify-pass planner on the host: tests/planner_check.cpp compiles the
-library's host code (csrc/wq_api.cpp) with the built kernel objects and
-replays, for the dense 64-layer pass and 400 random passes, the walk the
-persistent kernel makes over the plan, checking coverage and the
-blocked-split invariants.  No GPU is used."""
+"""The planners on the host: tests/planner_check.cpp compiles the library's
+host code (csrc/wq_api.cpp) with the built kernel objects and replays, for
+the dense 64-layer pass and 400 random passes, the walk the persistent
+kernel makes over the plan, checking coverage and the blocked-split
+invariants; and, for the single products and 3000 random shapes, the
+split-tile kernel's partition (every tile step once, slot and arrival
+bounds, parts per tile).  No GPU is used."""
 import os
 import shutil
 import subprocess
@@ -37,3 +39,5 @@ def test_planner_walk_covers_every_unit_once(tmp_path):
     assert r.returncode == 0 and tail.startswith("all ok"), r.stdout[-4000:] + r.stderr[-2000:]
     dense = [l for l in r.stdout.splitlines() if l.split()[0] == "dense64" and l.split()[1] != "plain" and "cus=256" in l]
     assert len(dense) == 3 and all("blocked mats=64" in l and "tasks=0" in l for l in dense), dense
+    split = [l for l in r.stdout.splitlines() if l.startswith("tile split:")]
+    assert split and "17408x5120: ok=1" in split[0] and "5120x17408: ok=1" in split[0], split
