@@ -144,10 +144,13 @@ wq_status wq_gemm_nvfp4_tiled(const uint8_t* tiled, float global_scale,
 
 /* wq_gemm_nvfp4_tiled without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc).  The split-K partial sums live in a
- * static device buffer of WQ_NOALLOC_SCRATCH_BYTES inside the library: one
- * per GPU, located on the first call on that GPU and held until the process
- * ends.  The call allocates nothing, on the host or the device.
+ * harnesses that forbid hipMalloc).  The workspace (arrival counters and
+ * partial sums) lives in a static device buffer of WQ_NOALLOC_SCRATCH_BYTES
+ * inside the library: one per GPU, located on the first call on that GPU
+ * and held until the process ends.  That first call also clears the
+ * counters, with a small kernel on `stream` ahead of the product; every
+ * product leaves them zero again.  The call allocates nothing, on the host
+ * or the device.
  * Results are those of wq_gemm_nvfp4_tiled with a workspace, bit for bit.
  * Errors: as wq_gemm_nvfp4_tiled, plus WQ_ERROR_SCRATCH_LIMIT (nothing
  * launched) when wq_gemm_workspace_bytes(WQ_FMT_NVFP4_TILED, M, K, N) exceeds
