@@ -637,6 +637,69 @@ def device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n, reps=10, warm=3):
     return out
 
 
+def valu_rows(wq, torch, stream, wl, host, mats_dev, plans, bytes_n, reps=5, check_rows=16):
+    """The MFMA/VALU comparison: the same prepared plans launched with the
+    NVFP4 steps on the matrix cores (wq_verify_launch) and on the vector
+    ALUs (wq_verify_launch_valu), alternating, HIP events per launch: the
+    dense pass at N = 2, 4, 8, and the 17408x5120 up-projection as a
+    one-matrix pass at N = 1, 2, 8.  The VALU outputs are checked against
+    the oracle on sampled rows (in the cpu_baseline leg)."""
+    dev = torch.device("cuda:0")
+    out = {"dense_pass": {}, "up_proj_17408x5120": {}}
+
+    def ab(plan, nbytes):
+        for _ in range(2):
+            wq.wq_verify_launch(plan, stream)
+            wq.wq_verify_launch_valu(plan, stream)
+        ev = {"mfma": [], "valu": []}
+        for _ in range(reps):
+            for kind, fn in (("mfma", wq.wq_verify_launch), ("valu", wq.wq_verify_launch_valu)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn(plan, stream)
+                b.record(stream)
+                ev[kind].append((a, b))
+        torch.cuda.synchronize()
+        r = {}
+        for kind in ("mfma", "valu"):
+            us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev[kind]]))
+            r[kind + "_us"] = us
+            r[kind + "_pct_of_8TBps"] = 100 * nbytes / us / 1e3 / PEAK_GBPS
+        r["valu_over_mfma"] = r["valu_us"] / r["mfma_us"]
+        return r
+
+    rng = np.random.default_rng(4545)
+    samples = []
+    for N in N_CYCLE:
+        out["dense_pass"][str(N)] = ab(plans[N], bytes_n[N])
+        # the last launch was the VALU one: sample its outputs of layer 0
+        for i in range(4):
+            spec, d = wl.matrices[i], host[i]
+            rows = np.unique(np.concatenate([rng.integers(0, spec.M, check_rows), [0, spec.M - 1]]))
+            y = mats_dev[i][3][:N].cpu().numpy()[:, rows].astype(np.float64)
+            samples.append((d.codes[rows], d.scales[rows], d.g, d.x[:N], y))
+    w1 = inputs.workload(1)
+    M, K = w1.matrices[0].M, w1.matrices[0].K
+    d = inputs.nvfp4_inputs(M, K, NMAX, w1.seed(0), w1.g, w1.x_scale)
+    t = torch.empty(wq.wq_nvfp4_tiled_bytes(M, K), dtype=torch.uint8, device=dev)
+    wq.wq_nvfp4_tile(torch.from_numpy(d.codes).to(dev), torch.from_numpy(d.scales).to(dev), t, stream)
+    x = torch.from_numpy(d.x.view(np.int16)).to(dev)
+    for N in (1, 2, 8):
+        y = torch.full((N, M), float("nan"), dtype=torch.float32, device=dev)
+        mats = [wq.Matrix(wq.WQ_FMT_NVFP4_TILED, M, K, t, None, x[:N], y, w1.g)]
+        ws = torch.zeros(wq.wq_verify_workspace_bytes(mats, N), dtype=torch.uint8, device=dev)
+        plan = wq.wq_verify_prepare(mats, N, ws, stream)
+        out["up_proj_17408x5120"][str(N)] = ab(plan, matrix_bytes("nvfp4", M, K, N))
+        rows = np.unique(np.concatenate([rng.integers(0, M, 4 * check_rows), [0, M - 1]]))
+        samples.append((d.codes[rows], d.scales[rows], w1.g, d.x[:N], y.cpu().numpy()[:, rows].astype(np.float64)))
+    out["parity_ok"] = None
+    out["max_err_over_bound"] = None
+    out["note"] = ("the verify-pass kernel with its NVFP4 step on the vector ALUs (stream_kernel<N, 8>) against the "
+                   "matrix cores (stream_kernel<N, 4>), same plans; valu_over_mfma > 1 means the matrix cores win")
+    PENDING.append((check_sampled_nvfp4, out, {"samples": samples}))
+    return out
+
+
 def chain_bytes(D, F, N, layers):
     """Bytes a chained MLP pass must move: per layer the NVFP4 gate, up and
     down weights (0.5625 B each), gamma (2D), the residual read and written
@@ -762,11 +825,13 @@ PROF_CMD = {
     "single": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/kts -o kts -- python3 bench.py "
               "--only-single --no-cpu-baseline",
     "chain": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/ktc -o ktc -- python3 bench.py "
-             "--steps 3 --warmup 1 --no-cpu-baseline --no-single --no-chain-single --check-rows 1 --workers 0",
+             "--steps 3 --warmup 1 --no-cpu-baseline --no-single --no-chain-single --no-valu --check-rows 1 --workers 0",
     "traffic_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- python3 "
-                     "bench.py --steps 6 --warmup 0 --no-cpu-baseline --no-single --no-chain --check-rows 1 --workers 0",
+                     "bench.py --steps 6 --warmup 0 --no-cpu-baseline --no-single --no-chain --no-valu --check-rows 1 "
+                     "--workers 0",
     "traffic_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- python3 "
-                     "bench.py --steps 6 --warmup 0 --no-cpu-baseline --no-single --no-chain --check-rows 1 --workers 0",
+                     "bench.py --steps 6 --warmup 0 --no-cpu-baseline --no-single --no-chain --no-valu --check-rows 1 "
+                     "--workers 0",
     "single_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcs_fetch -o fetch -- python3 "
                     "bench.py --only-single --no-cpu-baseline",
     "single_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcs_write -o write -- python3 "
@@ -846,8 +911,9 @@ def summarize_dense(args):
          "# stream_kernel<N, 4> is the tiled verify pass (the timed path of bench.py; one launch per pass, the",
          "# 64 down projections computed in LDS blocks, no reduction launch); stream_kernel<N, 0> the plain",
          "# row-major pass (reported as plain_layout) with its split-K reduce_kernel; stream_kernel_dyn the pass",
-         "# with N read on the device (per_n_device_count); probe_read_kernel<false> / <true> the read probe and",
-         "# the read-with-writes probe.  Durations in microseconds.", "",
+         "# with N read on the device (per_n_device_count); stream_kernel<N, 8> the same plans with the NVFP4",
+         "# steps on the vector ALUs (mfma_vs_valu); probe_read_kernel<false> / <true> the read probe and the",
+         "# read-with-writes probe.  Durations in microseconds.", "",
          "timed region of bench.py (the %d steps between its two synchronizations, %d per N):" % (steps, steps // 3),
          "%-36s %7s %12s %12s %12s %12s %9s" % ("kernel", "calls", "avg_us", "median_us", "min_us", "max_us",
                                                "%8TB_avg")]
@@ -861,6 +927,21 @@ def summarize_dense(args):
     tot = sum(algorithmic_bytes(wl, int(n.split("<")[1].split(",")[0])) for s, e, n in timed)
     L.append("%-36s %7d %12.1f %12.1f %12.1f %12.1f %9.1f" % (("all timed launches",) + _stats(v) + (
         100 * tot / (sum(v) * 1e3) / PEAK_GBPS,)))
+    # the MFMA/VALU comparison rows (mfma_vs_valu): the same plans with the
+    # NVFP4 steps on the vector ALUs (stream_kernel<N, 8>) and on the matrix
+    # cores (stream_kernel<N, 4>); passes longer than 1 ms are the dense
+    # pass, shorter ones the 17408x5120 one-matrix pass
+    if any(n.endswith(", 8>") for s_, e_, n in rows):
+        import statistics
+        L += ["", "matrix cores against vector ALUs (the mfma_vs_valu rows; median kernel durations, us):",
+              "%-28s %4s %12s %12s %10s" % ("pass", "N", "mfma_us", "valu_us", "valu/mfma")]
+        for label, big in (("dense 64-layer pass", True), ("17408x5120, one matrix", False)):
+            for N in range(1, 9):
+                mf = [(e - s_) / 1e3 for s_, e, n in rows if n == "wq::stream_kernel<%d, 4>" % N and ((e - s_) > 1e6) == big]
+                va = [(e - s_) / 1e3 for s_, e, n in rows if n == "wq::stream_kernel<%d, 8>" % N and ((e - s_) > 1e6) == big]
+                if mf and va:
+                    m, v = statistics.median(mf), statistics.median(va)
+                    L.append("%-28s %4d %12.1f %12.1f %10.2f" % (label, N, m, v, v / m))
     L += ["", "bench.py's own figures for the same run (HIP events on the launch stream):",
           "  roofline.avg_launch_us = %.1f; per_n us_per_pass_mean = %s" % (
               bl["roofline"]["avg_launch_us"],
@@ -1128,6 +1209,7 @@ def main():
     ap.add_argument("--only-single", action="store_true",
                     help="run only the probes and the single products (profiled runs of the single products)")
     ap.add_argument("--no-chain", action="store_true", help="skip the chained MLP pass")
+    ap.add_argument("--no-valu", action="store_true", help="skip the MFMA/VALU comparison rows")
     ap.add_argument("--no-chain-single", action="store_true",
                     help="skip the chain's single cooperative launch (kept out of rocprofv3 runs)")
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
@@ -1288,6 +1370,9 @@ def main():
     ok = True
 
     device_n = device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n)
+    valu = None
+    if not args.no_valu:
+        valu = valu_rows(wq, torch, stream, wl, host, mats_dev, plans, bytes_n)
     chained = None
     if not args.no_chain:
         chained = chain_rows(wq, torch, stream, wl, host, mats_dev, probe_gbps,
@@ -1332,6 +1417,7 @@ def main():
         # check, the CPU baseline and the roofline close the line
         "plain_layout": plain,
         "per_n_device_count": device_n,
+        "mfma_vs_valu": valu,
         "draft_step": draft,
         "chained_mlp": chained,
         "single_products": singles,
