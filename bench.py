@@ -960,14 +960,20 @@ def summarize_dense(args):
     return "\n".join(L) + "\n"
 
 
+def _is_main_single(n):
+    """The first kernel of a single-product call: the stream kernel, or the
+    split-tile kernel of the tiled products with few tiles per CU."""
+    return n.startswith("wq::stream_kernel<") or n.startswith("wq::split_kernel<")
+
+
 def _single_groups(rows, bl):
     """Assign the single products' dispatches to bench rows: each row made
     `calls` calls, back to back, in the order of the JSON; a call is one
-    stream kernel, then (split products) a reduce_kernel or (acceptance) an
-    accept_kernel."""
+    stream kernel or split kernel, then (chunked products) a reduce_kernel or
+    (acceptance) an accept_kernel."""
     main = []
     for s, e, n in rows:
-        if n.startswith("wq::stream_kernel<"):
+        if _is_main_single(n):
             main.append([n, (e - s) / 1e3, 0.0])
         elif n in ("wq::reduce_kernel", "wq::accept_kernel") and main:
             main[-1][2] += (e - s) / 1e3
@@ -980,7 +986,7 @@ def _single_groups(rows, bl):
             raise SystemExit("dispatches do not match the bench rows at %s N=%d %s" % (r["name"], r["N"], r["layout"]))
         out.append((r, names.pop(), [g[1] for g in grp], [g[2] for g in grp]))
     if i != len(main):
-        raise SystemExit("%d stream-kernel dispatches left over" % (len(main) - i))
+        raise SystemExit("%d stream- or split-kernel dispatches left over" % (len(main) - i))
     return out
 
 
@@ -1004,9 +1010,11 @@ def summarize_single(args):
          "#   " + _summary_cmd("single", args), "#",
          "# Each row: one (workload, layout, N) run of back-to-back calls over rotated weight copies (> 1 GiB);",
          "# layout accept: greedy acceptance fused on the tiled FP8 head (wq_head_accept), without / with logits;",
-         "# us = median stream-kernel duration plus median second kernel (reduce or accept) duration;",
+         "# kernel: split_kernel<N, fp8> for tiled products with fewer than 8 row tiles per CU (no second kernel),",
+         "# stream_kernel<N, mode> otherwise; us = median duration of that kernel plus median second kernel",
+         "# (reduce or accept) duration;",
          "# GB/s = algorithmic bytes / us; events_us = bench.py's HIP-event median per call (launch included).", "",
-         "%-44s %-14s %2s %-27s %6s %9s %8s %9s %8s %6s" % ("workload", "layout", "N", "kernel", "calls", "stream_us",
+         "%-44s %-14s %2s %-27s %6s %9s %8s %9s %8s %6s" % ("workload", "layout", "N", "kernel", "calls", "kernel_us",
                                                          "2nd_us", "events_us", "GB/s", "%8TB")]
     for r, name, d, d2 in _single_groups(rows, bl):
         sd, s2 = statistics.median(d), statistics.median(d2)
@@ -1071,7 +1079,7 @@ def summarize_single_traffic(args):
     def per_row(c):
         seq = []
         for n, x in c:
-            if n.startswith("wq::stream_kernel<"):
+            if _is_main_single(n):
                 seq.append([n, x])
             elif n in ("wq::reduce_kernel", "wq::accept_kernel") and seq:
                 seq[-1][1] += x
@@ -1080,7 +1088,7 @@ def summarize_single_traffic(args):
             out.append([x for _, x in seq[i:i + r["calls"]]])
             i += r["calls"]
         if i != len(seq):
-            raise SystemExit("%d stream-kernel dispatches left over" % (len(seq) - i))
+            raise SystemExit("%d stream- or split-kernel dispatches left over" % (len(seq) - i))
         return out
 
     pf, pw = per_row(fe), per_row(wr)
@@ -1089,7 +1097,7 @@ def summarize_single_traffic(args):
          "#   " + PROF_CMD["single_fetch"], "#   " + PROF_CMD["single_write"],
          "#   " + _summary_cmd("single-traffic", args), "#",
          "# Scale: FETCH_SIZE x%.4f, WRITE_SIZE x%.4f (the counters on wq_probe_copy of exactly 1 GiB)." % (fs, ws),
-         "# Per call (stream kernel plus its reduce or accept kernel, median over the row's calls): bytes after",
+         "# Per call (stream or split kernel plus its reduce or accept kernel, median over the row's calls): bytes after",
          "# scaling.  ratio = (fetch + write) / algorithmic bytes; a ratio under 0.98 is flagged (weights served",
          "# from a cache: the rotation over copies did not defeat the 256 MB last-level cache).", "",
          "%-44s %-14s %2s %12s %12s %14s %7s %s" % ("workload", "layout", "N", "fetch_B", "write_B", "algorithmic_B",
