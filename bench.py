@@ -1295,6 +1295,31 @@ def main():
     plans = {N: p for N, (p, _) in plans_t.items()}
     torch.cuda.synchronize()
 
+    bytes_n = {N: algorithmic_bytes(wl, N) for N in N_CYCLE}
+
+    # The reported-only rows that stream the same 12 GB run first: on a
+    # device that has been idle (generation, upload), the first ~30 passes
+    # run up to 20% slower and speed up pass by pass (kernel traces), which a
+    # few warm-up steps do not cover; these rows put ~180 ms of streaming
+    # ahead of the warm-up, so the timed region sees the steady state.
+
+    # the plain row-major layout (reported only)
+    plain = {}
+    for N in N_CYCLE:
+        p = plans_p[N][0]
+        for _ in range(2):
+            wq.wq_verify_launch(p, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(9):
+            wq.wq_verify_launch(p, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / 9 * 1e3
+        plain[str(N)] = {"us_per_pass": us, "gbps": bytes_n[N] / us / 1e3}
+
+    device_n = device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n)
+
     probe_gbps, write_probe = run_probes(wq, torch, stream)
 
     # warmup
@@ -1323,7 +1348,6 @@ def main():
 
     wall_s = t1 - t0
     durs = np.array([a.elapsed_time(b) * 1e-3 for a, b in ev])  # seconds per launch
-    bytes_n = {N: algorithmic_bytes(wl, N) for N in N_CYCLE}
     total_bytes = sum(bytes_n[N] for N in ns)
     value = total_bytes / wall_s / 1e9
     per_n = {}
@@ -1346,21 +1370,6 @@ def main():
                 "probe_read_gbps": probe_gbps, "frac_of_probe": achieved / probe_gbps,
                 "probe_write_cost": write_probe}
 
-    # the plain row-major layout, timed the same way (reported only)
-    plain = {}
-    for N in N_CYCLE:
-        p = plans_p[N][0]
-        for _ in range(2):
-            wq.wq_verify_launch(p, stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(9):
-            wq.wq_verify_launch(p, stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) / 9 * 1e3
-        plain[str(N)] = {"us_per_pass": us, "gbps": bytes_n[N] / us / 1e3}
-
     # parity: sampled rows of every matrix at every N (compared with the
     # oracle in the cpu_baseline leg)
     rng = np.random.default_rng(12345)
@@ -1377,7 +1386,6 @@ def main():
     PENDING.append((check_sampled_nvfp4, parity, {"samples": samples}))
     ok = True
 
-    device_n = device_n_rows(wq, torch, stream, wl, mats_dev, bytes_n)
     valu = None
     if not args.no_valu:
         valu = valu_rows(wq, torch, stream, wl, host, mats_dev, plans, bytes_n)
