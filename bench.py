@@ -443,7 +443,6 @@ def single_products(wq, torch, stream, probe_gbps, check_rows=2048):
         if wl.fmt == "fp8row":
             out += head_accept_rows(wq, torch, stream, wl, d, tiled, nt, rs, x8, probe_gbps)
         del tiled
-        torch.cuda.empty_cache()
     return out
 
 
@@ -545,7 +544,6 @@ def quantizer_rows(wq, torch, stream, probe_gbps, check_rows=64):
         PENDING.append((check_quantizer, row, {"name": name, "w": wh, "g": g, **got}))
         rows.append(row)
         del w
-        torch.cuda.empty_cache()
     return rows
 
 
@@ -1181,8 +1179,10 @@ def run_probes(wq, torch, stream):
     copy_dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     wq.wq_probe_copy(probe_buf[: 1 << 30], copy_dst, stream)
     torch.cuda.synchronize()
+    # the buffers go back to torch's cache, not to the driver: after a
+    # hipFree of these 5 GiB the dense pass ran 3% slower until the device
+    # next sat idle (measured: 1768 -> 1825 us at N = 2, for 60 passes)
     del probe_buf, copy_dst
-    torch.cuda.empty_cache()
     return probe_gbps, write_probe
 
 
@@ -1298,10 +1298,10 @@ def main():
     bytes_n = {N: algorithmic_bytes(wl, N) for N in N_CYCLE}
 
     # The reported-only rows that stream the same 12 GB run first: on a
-    # device that has been idle (generation, upload), the first ~30 passes
-    # run up to 20% slower and speed up pass by pass (kernel traces), which a
-    # few warm-up steps do not cover; these rows put ~180 ms of streaming
-    # ahead of the warm-up, so the timed region sees the steady state.
+    # device that has been idle (generation, upload), the first ~10 passes
+    # run up to 25% slower while its clocks come up (measured: 2500, 2144,
+    # 2032, ... 1966 us at N = 8), more than a few warm-up steps cover;
+    # these rows put ~180 ms of streaming ahead of the warm-up.
 
     # the plain row-major layout (reported only)
     plain = {}
