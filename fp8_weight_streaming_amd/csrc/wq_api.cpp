@@ -996,10 +996,18 @@ wq_status wq_mlp_chain_launch_persistent(const wq_mlp_plan* plan, void* stream) 
     return WQ_ERROR_INVALID_VALUE;
   if (plan->grid_chain == 0) return WQ_ERROR_UNSUPPORTED_SHAPE;
   char* ws = static_cast<char*>(plan->workspace);
+  // the launches' range tables (down's aligned to its K chunks) when they
+  // were built for as many workgroups as the single launch has, else equal
+  // splits
+  const bool same_grid = plan->grid_gate_up == plan->grid_chain && plan->grid_down == plan->grid_chain &&
+                         plan->ranges_gate_up_offset < plan->workspace_bytes &&
+                         plan->ranges_down_offset < plan->workspace_bytes;
+  const WgRange* rgu = same_grid ? reinterpret_cast<const WgRange*>(ws + plan->ranges_gate_up_offset) : nullptr;
+  const WgRange* rdn = same_grid ? reinterpret_cast<const WgRange*>(ws + plan->ranges_down_offset) : nullptr;
   const hipError_t e = launch_chain_persistent(plan->N, reinterpret_cast<const DevMat*>(ws),
                                                reinterpret_cast<ChainCtl*>(ws + plan->ctl_offset), plan->h,
                                                reinterpret_cast<float*>(ws + plan->ssp_offset), plan->layers, plan->D,
-                                               plan->grid_chain, static_cast<hipStream_t>(stream));
+                                               plan->grid_chain, rgu, rdn, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WQ_SUCCESS : WQ_ERROR_LAUNCH;
 }
 

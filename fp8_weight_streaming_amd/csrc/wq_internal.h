@@ -212,11 +212,13 @@ constexpr int waves_for_mode(int mode) {
 constexpr int kChainThreads = 256;
 
 // Grid barrier of the single-launch chain (in the workspace, zero before
-// the first launch): arrivals of the current barrier, barriers completed,
-// and a sticky flag set if a wait gave up (see kSpinLimit).
+// the first launch): arrivals so far in this launch (barrier b is open once
+// count reaches b times the grid), workgroups finished (the last one sets
+// both back to zero), and a sticky flag set if a wait gave up (see
+// kSpinLimit).
 struct ChainCtl {
   uint32_t count;
-  uint32_t gen;
+  uint32_t done;
   uint32_t error;
   uint32_t pad;
 };
@@ -258,8 +260,11 @@ hipError_t launch_stream_dyn(const DevMat* mats, const WgRange* ranges, const in
 // ssp only.
 hipError_t launch_chain_reduce(float* h, const DevMat* down, int D, int N, float* ssp, hipStream_t stream);
 // All layers of a chain in one cooperative launch of `grid` workgroups.
+// ranges_gate_up / ranges_down: the workgroups' unit ranges of the two
+// streaming phases (built for `grid` workgroups), or null for equal splits.
 hipError_t launch_chain_persistent(int N, const DevMat* mats, ChainCtl* ctl, float* h, float* ssp, int layers, int D,
-                                   int grid, hipStream_t stream);
+                                   int grid, const WgRange* ranges_gate_up, const WgRange* ranges_down,
+                                   hipStream_t stream);
 // Workgroups of the single-launch chain that fit on the device at once.
 int chain_persistent_blocks_per_cu(int N);
 // Host-side argument checks of the single-matrix products (no HIP call).

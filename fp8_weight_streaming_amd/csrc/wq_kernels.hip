@@ -108,6 +108,12 @@ __device__ __forceinline__ void bstore2(uint32_t v, __amdgpu_buffer_rsrc_t r, ui
 // A buffer offset past every output buffer (outputs are < 2 GiB): the
 // hardware range check drops stores there.
 constexpr uint32_t kDropOffset = 0x80000000u;
+// Device-scope (sc1) loads: they take no line from a cache that another XCD
+// may not see, so they return what a write-through store of any workgroup
+// left in memory once that store has completed.  With write-through stores
+// on the other side, data passes between workgroups of one launch with no
+// L2 writeback or invalidate (the single-launch chain's phases).
+constexpr int kAuxCoherent = 16;
 
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAuxStream));
@@ -205,7 +211,7 @@ __device__ void stage_x(char* lds, const uint16_t* __restrict__ x, int K, int k0
 // the way, so a chunk of any size is one round trip, where staging through
 // registers (eight 16-byte loads per thread per round) took two or three
 // at N = 8.  The caller waits for the loads and synchronizes.
-template <int N>
+template <int N, int AUX = 0>
 __device__ __forceinline__ void stage_x_direct(char* lds, const uint16_t* __restrict__ x, int K, int k0, int klen,
                                                int kc_pad) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc_uniform(x, (uint64_t)N * (uint64_t)K * 2u);
@@ -220,7 +226,7 @@ __device__ __forceinline__ void stage_x_direct(char* lds, const uint16_t* __rest
     const uint32_t off = kc < valid ? (uint32_t)((n * K + k0 + 8 * kc) * 2) : 0x80000000u;
     if (q < total)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(lds + (size_t)q0 * 16), 16,
-                                               off, 0, 0, 0);
+                                               off, 0, 0, AUX);
   }
 }
 
@@ -253,11 +259,14 @@ struct NormBatch {
   u32x4 gm[kNormLoads];
   float ss;
 };
-template <int N>
+// COH: h and its partial sums of squares were written in the same launch
+// (the single-launch chain), so they are read with device-scope loads.
+template <int N, bool COH>
 __device__ __forceinline__ void norm_load(NormBatch& b, const DevMat& mt, int kc_pad, int p0) {
   const int K = mt.K;
   const int valid = K / 8;
   const int total = kc_pad * N;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc_uniform(mt.h, (uint64_t)N * (uint64_t)K * 4u);
 #pragma unroll
   for (int j = 0; j < kNormLoads; ++j) {
     const int p = p0 + j * (int)blockDim.x;
@@ -266,18 +275,30 @@ __device__ __forceinline__ void norm_load(NormBatch& b, const DevMat& mt, int kc
     b.h1[j] = b.h0[j];
     b.gm[j] = u32x4{0u, 0u, 0u, 0u};
     if (p < total && kc < valid) {
-      const float* hp = mt.h + (size_t)n * K + 8 * kc;
-      b.h0[j] = *reinterpret_cast<const f32x4*>(hp);
-      b.h1[j] = *reinterpret_cast<const f32x4*>(hp + 4);
+      if constexpr (COH) {
+        const uint32_t off = (uint32_t)((n * K + 8 * kc) * 4);
+        b.h0[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)off, 0, kAuxCoherent));
+        b.h1[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)off + 16, 0, kAuxCoherent));
+      } else {
+        const float* hp = mt.h + (size_t)n * K + 8 * kc;
+        b.h0[j] = *reinterpret_cast<const f32x4*>(hp);
+        b.h1[j] = *reinterpret_cast<const f32x4*>(hp + 4);
+      }
       b.gm[j] = *reinterpret_cast<const u32x4*>(mt.gamma + 8 * kc);
     }
   }
 }
-template <int N>
+template <int N, bool COH>
 __device__ __forceinline__ void norm_first(NormBatch& b, const DevMat& mt, int kc_pad) {
   const int wv = (int)(threadIdx.x >> 6), ln = (int)(threadIdx.x & 63);
-  b.ss = (wv < N && ln < mt.nparts) ? mt.ssp[(size_t)wv * mt.nparts + ln] : 0.0f;
-  norm_load<N>(b, mt, kc_pad, (int)threadIdx.x);
+  if constexpr (COH) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc_uniform(mt.ssp, (uint64_t)N * (uint64_t)mt.nparts * 4u);
+    const uint32_t off = (wv < N && ln < mt.nparts) ? (uint32_t)((wv * mt.nparts + ln) * 4) : kDropOffset;
+    b.ss = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, kAuxCoherent));
+  } else {
+    b.ss = (wv < N && ln < mt.nparts) ? mt.ssp[(size_t)wv * mt.nparts + ln] : 0.0f;
+  }
+  norm_load<N, COH>(b, mt, kc_pad, (int)threadIdx.x);
 }
 template <int N>
 __device__ __forceinline__ void norm_store(const NormBatch& b, char* lds, const DevMat& mt, int kc_pad, int p0,
@@ -307,7 +328,7 @@ __device__ __forceinline__ void norm_store(const NormBatch& b, char* lds, const 
   }
 }
 // Everything after norm_first (every thread calls it; it holds a barrier).
-template <int N>
+template <int N, bool COH>
 __device__ void stage_norm(NormBatch& b, char* lds, const DevMat& mt, int kc_pad, int64_t u0, int64_t u1,
                            int64_t units) {
   float* rl = reinterpret_cast<float*>(lds + kZeroOffset<N>() + kZeroBytes<N>());
@@ -326,7 +347,7 @@ __device__ void stage_norm(NormBatch& b, char* lds, const DevMat& mt, int kc_pad
   norm_store<N>(b, lds, mt, kc_pad, (int)threadIdx.x, rl, u0, u1, units);
   for (int p0 = (int)threadIdx.x + kNormLoads * (int)blockDim.x; p0 < kc_pad * N;
        p0 += kNormLoads * (int)blockDim.x) {
-    norm_load<N>(b, mt, kc_pad, p0);
+    norm_load<N, COH>(b, mt, kc_pad, p0);
     norm_store<N>(b, lds, mt, kc_pad, p0, rl, u0, u1, units);
   }
 }
@@ -1199,53 +1220,65 @@ __device__ void fp8_unit(const DevMat& mt, int chunk, int tile, const char* lds)
 // ---- grid barrier of the single-launch chain --------------------------------
 // A split barrier: a workgroup arrives once its stores of a phase are
 // issued and waits, later, before it reads what the other workgroups stored
-// (so that it can issue its next weight loads in between).  count holds the
-// arrivals at the open barrier; the last arrival resets it and advances gen,
-// which the waiting workgroups watch.  Every wait is bounded: after
-// kSpinLimit polls it sets ctl->error and goes on, so that the grid always
-// drains even if a workgroup never arrives (the results are then not
-// defined).  Only a launch that keeps every workgroup resident (a
-// cooperative launch) may use it.
+// (so that it can issue its next weight loads in between).  ctl->count
+// counts every arrival of the launch; a workgroup's b-th wait ends once the
+// count has reached b times the grid (its target, kept in LDS), so the
+// barrier costs the last arrival's one atomic and the waiters' next poll.
+// Every wait is bounded: after kSpinLimit polls it sets ctl->error and goes
+// on, so that the grid always drains even if a workgroup never arrives (the
+// results are then not defined).  Only a launch that keeps every workgroup
+// resident (a cooperative launch) may use it.  grid_finish, after a
+// workgroup's last wait, counts it out; the last one sets count and done
+// back to zero for the next launch (every other workgroup has passed every
+// wait by then).
+//
+// There are no fences.  Everything one phase hands to the next (s, the
+// down sums, h, the sums of squares) is stored through the L2 and read with
+// device-scope loads (kAuxCoherent), so it never sits in a cache another
+// XCD cannot see; an arrival is counted only after the workgroup's stores
+// have completed (s_waitcnt), and a waiting workgroup issues its reads
+// only after it has seen the barrier open.  An agent-scope release fence
+// is a writeback of the XCD's whole L2: per-workgroup timelines showed the
+// last arrival landing 15-20 us after the workgroup's stores had drained.
 struct GridSync {
   ChainCtl* ctl;
-  uint32_t* s_gen;  // LDS: gen as read at this workgroup's last arrival
+  uint32_t* s_target;  // LDS: the count that opens this workgroup's next wait
 };
 constexpr uint32_t kSpinLimit = 1u << 19;
 
-// Every wave first waits for its own stores to be performed (a workgroup
-// barrier alone does not wait for global stores); then one release fence
-// per workgroup, by thread 0, makes them all visible device-wide (a fence
-// per wave cost each barrier thousands of cache write-backs).
 __device__ __forceinline__ void grid_arrive(const GridSync& gs) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+  __syncthreads();                // ... and every other wave's
   if (threadIdx.x == 0) {
-    ChainCtl* c = gs.ctl;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    *gs.s_gen = __hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (__hip_atomic_fetch_add(&c->count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
-      __hip_atomic_store(&c->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&c->gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    *gs.s_target += gridDim.x;
+    __hip_atomic_fetch_add(&gs.ctl->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 __device__ __forceinline__ void grid_wait(const GridSync& gs) {
   if (threadIdx.x == 0) {
     ChainCtl* c = gs.ctl;
-    const uint32_t g = *gs.s_gen;
-    // (relaxed polls, so that a poll does not invalidate the caches; the
-    // acquire fence below orders what follows after the change was seen)
-    for (uint32_t it = 0; __hip_atomic_load(&c->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g; ++it) {
+    const uint32_t target = *gs.s_target;
+    // (relaxed device-scope polls: each reads the counter from memory)
+    for (uint32_t it = 0; __hip_atomic_load(&c->count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++it) {
       if (it == kSpinLimit) {
         __hip_atomic_fetch_or(&c->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void grid_finish(const GridSync& gs) {
+  if (threadIdx.x == 0) {
+    ChainCtl* c = gs.ctl;
+    if (__hip_atomic_fetch_add(&c->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
+      __hip_atomic_store(&c->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&c->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // ---- the persistent kernel -------------------------------------------------
@@ -1368,6 +1401,10 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
       } else if constexpr (MODE == kModeTiled || MODE == kModeTiledArgmax || MODE == kModeTiledValu) {
         stage_x_direct<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads (and every older one) are done
+      } else if constexpr (SYNC) {
+        // X (s) was written earlier in this launch: device-scope loads
+        stage_x_direct<N, kAuxCoherent>(lds, mt.x, mt.K, k0, klen, kc_pad);
+        __builtin_amdgcn_s_waitcnt(0);
       } else {
         stage_x<N>(lds, mt.x, mt.K, k0, klen, kc_pad);
       }
@@ -1401,12 +1438,13 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
     } else if constexpr (MODE == kModeTiledGlu) {
       NormBatch nb;
       auto pre_norm = [&]() {
-        if constexpr (!SYNC) norm_first<N>(nb, mt, kc_pad);
+        if constexpr (!SYNC) norm_first<N, false>(nb, mt, kc_pad);
       };
       auto stage_norm_x = [&]() {
         sync_first();
-        if constexpr (SYNC) norm_first<N>(nb, mt, kc_pad);
-        stage_norm<N>(nb, lds, mt, kc_pad, first - mt.unit0, run_end - mt.unit0, (int64_t)mt.nchunks * mt.ntiles);
+        if constexpr (SYNC) norm_first<N, true>(nb, mt, kc_pad);
+        stage_norm<N, SYNC>(nb, lds, mt, kc_pad, first - mt.unit0, run_end - mt.unit0,
+                            (int64_t)mt.nchunks * mt.ntiles);
         __syncthreads();
       };
       tiled_run<N, kPrefetchWide, false, kEpiGlu, false>(mt, chunk, share0, share1, ubase, -1, lds, bestk, pre_norm,
@@ -1552,15 +1590,27 @@ __global__ __launch_bounds__(kThreadsTiled) void stream_kernel_dyn(const DevMat*
 // in order), so every run gives the same bits.
 // The work of block (p, n) as above, by threads 0 .. kChainThreads - 1 of the
 // calling workgroup (every thread calls it: it holds two barriers).
+// COH (the single-launch chain): the down sums and h are read with
+// device-scope loads and h and ssp written through the L2, since other
+// workgroups of the same launch read and wrote them.
+template <bool COH>
 __device__ __forceinline__ void chain_reduce_block(float* __restrict__ h, const DevMat* __restrict__ down, int D,
                                                    int N, int n, int p, int P, float* __restrict__ ssp,
                                                    float* wsum) {
   const int t = (int)threadIdx.x;
   const int m = p * kChainThreads + t;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h, (uint64_t)N * (uint64_t)D * 4u);
+  auto ld = [&](const float* base, uint64_t elems, size_t i) -> float {
+    if constexpr (COH)
+      return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(base, elems * 4u), (int)(i * 4), 0,
+                                                                  kAuxCoherent));
+    else
+      return base[i];
+  };
   float v = 0.0f;
   if (t < kChainThreads && m < D) {
     const size_t o = (size_t)n * D + m;
-    v = h[o];
+    v = ld(h, (uint64_t)N * D, o);
     if (down) {
       const int nchunks = down->nchunks;
       float acc = 0.0f;
@@ -1571,17 +1621,20 @@ __device__ __forceinline__ void chain_reduce_block(float* __restrict__ h, const 
           float v[kBatch];
 #pragma unroll
           for (int j = 0; j < kBatch; ++j)
-            v[j] = c0 + j < nchunks ? down->part[(size_t)(c0 + j) * N * D + o] : 0.0f;
+            v[j] = c0 + j < nchunks ? ld(down->part, (uint64_t)nchunks * N * D, (size_t)(c0 + j) * N * D + o) : 0.0f;
 #pragma unroll
           for (int j = 0; j < kBatch; ++j)
             if (c0 + j < nchunks) acc += v[j];
         }
         acc = down->g * acc;
       } else {
-        acc = down->y[o];
+        acc = ld(down->y, (uint64_t)N * D, o);
       }
       v = v + acc;
-      h[o] = v;
+      if constexpr (COH)
+        bstore4(v, rh, (uint32_t)(o * 4));
+      else
+        h[o] = v;
     }
   }
   float sq = v * v;
@@ -1592,7 +1645,10 @@ __device__ __forceinline__ void chain_reduce_block(float* __restrict__ h, const 
   if (t == 0) {
     float s = 0.0f;
     for (int w = 0; w < kChainThreads / 64; ++w) s += wsum[w];
-    ssp[(size_t)n * P + p] = s;
+    if constexpr (COH)
+      bstore4(s, make_rsrc(ssp, (uint64_t)N * P * 4u), (uint32_t)((n * P + p) * 4));
+    else
+      ssp[(size_t)n * P + p] = s;
   }
   __syncthreads();
 }
@@ -1601,7 +1657,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_reduce_kernel(float* __re
                                                                      const DevMat* __restrict__ down, int D, int N,
                                                                      float* __restrict__ ssp) {
   __shared__ float wsum[kChainThreads / 64];
-  chain_reduce_block(h, down, D, N, blockIdx.y, blockIdx.x, gridDim.x, ssp, wsum);
+  chain_reduce_block<false>(h, down, D, N, blockIdx.y, blockIdx.x, gridDim.x, ssp, wsum);
 }
 
 // ---- a whole chain in one launch ------------------------------------------------
@@ -1614,25 +1670,29 @@ __global__ __launch_bounds__(kChainThreads) void chain_reduce_kernel(float* __re
 template <int N>
 __global__ __launch_bounds__(kThreads) void chain_kernel(const DevMat* __restrict__ mats, ChainCtl* ctl,
                                                          float* __restrict__ h, float* __restrict__ ssp, int layers,
-                                                         int D) {
+                                                         int D, const WgRange* __restrict__ ranges_gate_up,
+                                                         const WgRange* __restrict__ ranges_down) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ uint32_t s_gen;
+  __shared__ uint32_t s_target;
   __shared__ float wsum[kChainThreads / 64];
-  const GridSync gs{ctl, &s_gen};
+  if (threadIdx.x == 0) s_target = 0;  // (only thread 0 reads or writes it)
+  const GridSync gs{ctl, &s_target};
   const int P = (D + kChainThreads - 1) / kChainThreads;
   const DevMat none{};
-  for (int b = blockIdx.x; b < N * P; b += gridDim.x) chain_reduce_block(h, nullptr, D, N, b / P, b % P, P, ssp, wsum);
+  for (int b = blockIdx.x; b < N * P; b += gridDim.x)
+    chain_reduce_block<true>(h, nullptr, D, N, b / P, b % P, P, ssp, wsum);
   grid_arrive(gs);
   for (int l = 0; l < layers; ++l) {
-    stream_body<N, kModeTiledGlu, true>(mats + 2 * l, nullptr, none, lds, &gs);
+    stream_body<N, kModeTiledGlu, true>(mats + 2 * l, ranges_gate_up, none, lds, &gs);
     grid_arrive(gs);
-    stream_body<N, kModeTiledWide, true>(mats + 2 * l + 1, nullptr, none, lds, &gs);
+    stream_body<N, kModeTiledWide, true>(mats + 2 * l + 1, ranges_down, none, lds, &gs);
     grid_arrive(gs);
     grid_wait(gs);
     for (int b = blockIdx.x; b < N * P; b += gridDim.x)
-      chain_reduce_block(h, mats + 2 * l + 1, D, N, b / P, b % P, P, ssp, wsum);
+      chain_reduce_block<true>(h, mats + 2 * l + 1, D, N, b / P, b % P, P, ssp, wsum);
     if (l + 1 < layers) grid_arrive(gs);
   }
+  grid_finish(gs);
 }
 
 hipError_t launch_chain_reduce(float* h, const DevMat* down, int D, int N, float* ssp, hipStream_t stream) {
@@ -1711,10 +1771,10 @@ static std::atomic<uint64_t>& chain_lds_set() {
 
 template <int N>
 static hipError_t launch_chain_n(const DevMat* mats, ChainCtl* ctl, float* h, float* ssp, int layers, int D, int grid,
-                                 hipStream_t stream) {
+                                 const WgRange* rgu, const WgRange* rdn, hipStream_t stream) {
   hipError_t e = allow_lds(reinterpret_cast<const void*>(&chain_kernel<N>), chain_lds_set<N>());
   if (e != hipSuccess) return e;
-  void* args[] = {&mats, &ctl, &h, &ssp, &layers, &D};
+  void* args[] = {&mats, &ctl, &h, &ssp, &layers, &D, &rgu, &rdn};
   return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&chain_kernel<N>), dim3(grid), dim3(kThreads), args,
                                     lds_bytes_for(N) + kArgLdsBytes, stream);
 }
@@ -1730,16 +1790,16 @@ static int chain_blocks_n() {
 }
 
 hipError_t launch_chain_persistent(int N, const DevMat* mats, ChainCtl* ctl, float* h, float* ssp, int layers, int D,
-                                   int grid, hipStream_t stream) {
+                                   int grid, const WgRange* rgu, const WgRange* rdn, hipStream_t stream) {
   switch (N) {
-    case 1: return launch_chain_n<1>(mats, ctl, h, ssp, layers, D, grid, stream);
-    case 2: return launch_chain_n<2>(mats, ctl, h, ssp, layers, D, grid, stream);
-    case 3: return launch_chain_n<3>(mats, ctl, h, ssp, layers, D, grid, stream);
-    case 4: return launch_chain_n<4>(mats, ctl, h, ssp, layers, D, grid, stream);
-    case 5: return launch_chain_n<5>(mats, ctl, h, ssp, layers, D, grid, stream);
-    case 6: return launch_chain_n<6>(mats, ctl, h, ssp, layers, D, grid, stream);
-    case 7: return launch_chain_n<7>(mats, ctl, h, ssp, layers, D, grid, stream);
-    case 8: return launch_chain_n<8>(mats, ctl, h, ssp, layers, D, grid, stream);
+    case 1: return launch_chain_n<1>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
+    case 2: return launch_chain_n<2>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
+    case 3: return launch_chain_n<3>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
+    case 4: return launch_chain_n<4>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
+    case 5: return launch_chain_n<5>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
+    case 6: return launch_chain_n<6>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
+    case 7: return launch_chain_n<7>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
+    case 8: return launch_chain_n<8>(mats, ctl, h, ssp, layers, D, grid, rgu, rdn, stream);
     default: return hipErrorInvalidValue;
   }
 }
