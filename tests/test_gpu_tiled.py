@@ -418,3 +418,32 @@ def test_blocked_split_three_chunks_dense_down_shape(wq):
         else:
             print("%s: single-matrix split %s differs from the blocked split: bitwise comparison skipped"
                   % (f, wq.wq_gemm_split(fmt, d.M, d.K)), flush=True)
+
+
+def test_split_tile_calls_share_one_workspace(wq):
+    """Single products of the split-tile kernel (few row tiles, K cut into
+    several chunks whose parts the last workgroup to arrive adds) called
+    back to back on ONE workspace, zeroed once: every call must read the
+    parts of its own call (the shapes are small, so earlier calls' parts
+    and counters are still in the caches), match the oracle, and leave the
+    arrival counters at zero."""
+    shapes = [(32, 16384), (48, 8736), (16, 4096), (40, 17440)]
+    data = [inputs.nvfp4_inputs(M, K, 8, seed=700 + M + K, g=0.02) for M, K in shapes]
+    plans = [wq.wq_gemm_split(wq.WQ_FMT_NVFP4_TILED, M, K) for M, K in shapes]
+    print("split-tile shapes %s plans %s" % (shapes, plans), flush=True)
+    assert all(kc == 0 for kc, _ in plans) and any(nc > 1 for _, nc in plans)
+    tiled = [to_tiled(wq, d) for d in data]
+    nbytes = max(wq.wq_gemm_workspace_bytes(wq.WQ_FMT_NVFP4_TILED, M, K, 8) for M, K in shapes)
+    ws = workspace(nbytes)
+    rng = np.random.default_rng(71)
+    for rep in range(3):
+        for (M, K), d, t in zip(shapes, data, tiled):
+            N = (8, 3, 5)[rep]
+            x = inputs.to_bf16(rng.standard_normal((N, K)).astype(np.float32))
+            y = torch.full((N, M), float("nan"), dtype=torch.float32, device=DEV)
+            wq.wq_gemm_nvfp4_tiled(t, d.g, dev_bf16bits(x), y, M, K, ws)
+            torch.cuda.synchronize()
+            yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, x)
+            assert_close(y.cpu().numpy(), yr, ar, "repeat %d M=%d K=%d N=%d" % (rep, M, K, N))
+    counters = ws[:16384].cpu().numpy()
+    assert not counters.any(), "arrival counters not left at zero"
