@@ -133,9 +133,12 @@ Split gemm_split(int fmt, int M, int K, int cus) {
 // one equal piece per wave; with C > 1, every tile's C parts are added in
 // chunk order by the workgroup whose part arrives last.  s is chosen by the
 // bytes the busiest CU moves at N = 8 (the most X): the weights of its run,
-// its X chunk and, for C > 1, the parts written and read (512 bytes each
-// way) plus the arrival round trips at the end (taken as 128 KB of
-// streaming, and 2 KB more per chunk).
+// its X chunk (mostly served by the L2: counted at half weight) and, for
+// C > 1, the parts written and read (512 bytes each way) plus the arrival
+// round trips at the end (taken as 128 KB of streaming, and 8 KB more per
+// chunk).  Fitted to sweeps of s on MI355X: 5120 x 17408 at N = 8 took
+// 17.96 / 16.96 / 16.72 / 17.28 / 18.56 us with 8 / 6 / 4 / 3 / 2 chunks,
+// 17408 x 5120 at N = 1 14.0 / 17.8 / 18.0 us with 1 / 2 / 3.
 // Nothing depends on N, so neither do the results' bits.
 struct TileSplit {
   bool ok = false;
@@ -163,12 +166,12 @@ TileSplit tile_split_plan(int fmt, int M, int K, int cus) {
     if (G < C) continue;
     const int64_t tiles_max = ceil_div(T, G / C);  // a chunk gets at least G / C workgroups
     const int64_t run_max = tiles_max * s;
-    const double tail = C > 1 ? (double)(T * C) * 1024.0 / (double)G + 131072.0 + 2048.0 * (double)C : 0.0;
+    const double tail = C > 1 ? (double)(T * C) * 1024.0 / (double)G + 131072.0 + 8192.0 * (double)C : 0.0;
     const int64_t smin = std::min(s, sl);
     const int64_t slots = ceil_div(ceil_div(run_max, W), smin) + 1;
     if (tiles_max > kSplitArrivalsMax) continue;
     if (lds_bytes_for(8) + (uint64_t)W * slots * kSplitPartBytes + kSplitStaticLds > 160u * 1024u) continue;
-    const double cost = (double)run_max * step_bytes + 16.0 * (double)(s * sk) + tail;
+    const double cost = (double)run_max * step_bytes + 8.0 * (double)(s * sk) + tail;
     if (cost < best) {
       best = cost;
       p.ok = true;
