@@ -1094,13 +1094,18 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(DevMat mt, uint32_
     __syncthreads();
     // per tile of the run: the sums of the waves that touched it, in wave
     // order (every wave's slot read issued before the additions)
-    const int my_t0 = s_tile0[lane & (kW - 1)], my_t1 = s_tile1[lane & (kW - 1)];
+    int wt0[kW], wt1[kW];
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      wt0[w] = s_tile0[w];
+      wt1[w] = s_tile1[w];
+    }
     for (int t = ta + wave; t < tb; t += kW) {
       f32x4 v[kW];
       bool use[kW];
 #pragma unroll
       for (int w = 0; w < kW; ++w) {
-        const int t0 = __shfl(my_t0, w), t1 = __shfl(my_t1, w);
+        const int t0 = wt0[w], t1 = wt1[w];
         use[w] = t >= t0 && t <= t1;
         const int j = use[w] ? t - t0 : 0;
         v[w] = *reinterpret_cast<const f32x4*>(slots + ((size_t)w * slots_per_wave + j) * 512 + 16 * (lane & 31));
