@@ -202,6 +202,9 @@ def wq_status_string(status: int) -> str:
 
 
 def wq_gemm_workspace_bytes(fmt: int, M: int, K: int, N: int) -> int:
+    """Workspace bytes of a single-matrix call (0: none).  Allocate it zeroed
+    (torch.zeros): its first 16 KiB are arrival counters that every call
+    leaves at zero, so one buffer serves any later single-matrix call."""
     return int(_lib.wq_gemm_workspace_bytes(fmt, M, K, N))
 
 
