@@ -244,6 +244,13 @@ constexpr int kSplitChunksMax = 24;
 // Threads per workgroup of the split kernel, and steps in flight per lane.
 constexpr int kSplitThreads = 512;
 constexpr int kSplitPrefetch = 3;
+// Tiled-stream outputs held until the chip-wide 100 MHz clock enters a new
+// window of 2^kDeferWindowBits ticks (10.24 us), from kDeferMinN columns up.
+// Measured over the dense 64-layer pass (us per pass at N = 2 / 4 / 8):
+// written at once 1783 / 1870 / 2030; windows of 5.12 us 1793 / 1860 /
+// 1923, 10.24 us 1793 / 1840 / 1899, 20.48 us 1794 / 1855 / 1939.
+constexpr int kDeferWindowBits = 10;
+constexpr int kDeferMinN = 4;
 // LDS the split kernel declares statically (its arrival lists), kept free
 // of its dynamic LDS.
 constexpr uint32_t kSplitStaticLds = 1024;

@@ -698,6 +698,18 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
   float prev[4] = {0.f, 0.f, 0.f, 0.f};
   uint32_t so[4] = {kDropOffset, kDropOffset, kDropOffset, kDropOffset};
+  // Deferred outputs (N >= kDeferMinN): an emitted pair is held in psum /
+  // pso and written at the first step on which the chip-wide 100 MHz clock
+  // has entered a new window of 2^kDeferWindowBits ticks, or at the end of
+  // the next tile, whichever comes first.  Waves all over the chip then
+  // write in the same short intervals instead of at random moments: writes
+  // that reach memory while reads stream past cost a read/write turnaround
+  // each when they arrive alone, far less when they arrive together.
+  constexpr bool kDefer = EPI == kEpiStore && N >= kDeferMinN;
+  float psum[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t pso[4] = {kDropOffset, kDropOffset, kDropOffset, kDropOffset};
+  bool pending = false;
+  uint32_t pwin = 0;
 
   // next step to compute: tile ci, step cst
   int ci = 0, cst = 0;
@@ -808,12 +820,33 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       }
       if (to_lds && lane < 32) *reinterpret_cast<f32x4*>(lds + poff) = pout;
     }
+    if constexpr (kDefer) {
+      // the same min(N, 4) stores on every step; real offsets only when the
+      // held pair is written (a new window, the end of a tile, or a new pair
+      // to hold)
+      const uint32_t win = (uint32_t)(__builtin_amdgcn_s_memrealtime() >> kDeferWindowBits);
+      const bool emit_now = fin && so[0] != kDropOffset;
+      const bool fl = pending && (win != pwin || fin);
 #pragma unroll
-    for (int r = 0; r < kStores; ++r) {
-      if constexpr (EPI == kEpiGlu)
-        bstore2(sbits[r], ro, fin ? so[r] : kDropOffset);
-      else
-        bstore4(sum[r], ro, fin ? so[r] : kDropOffset);
+      for (int r = 0; r < kStores; ++r) bstore4(psum[r], ro, fl ? pso[r] : kDropOffset + 4u * r);
+      if (fl) pending = false;
+      if (emit_now) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          psum[r] = sum[r];
+          pso[r] = so[r];
+        }
+        pending = true;
+        pwin = win;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < kStores; ++r) {
+        if constexpr (EPI == kEpiGlu)
+          bstore2(sbits[r], ro, fin ? so[r] : kDropOffset);
+        else
+          bstore4(sum[r], ro, fin ? so[r] : kDropOffset);
+      }
     }
     if (++cst == nst) { cst = 0; ++ci; }
   };
@@ -847,6 +880,13 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
 #pragma unroll
   for (int i = 0; i < PF; ++i)
     if (q0 + i < Q) compute_next(i);
+  if constexpr (kDefer) {
+    // the last pair of the run, if still held
+    if (pending) {
+#pragma unroll
+      for (int r = 0; r < kStores; ++r) bstore4(psum[r], ro, pso[r]);
+    }
+  }
 }
 
 // ---- single products with few tiles per CU: tiles split across waves --------
