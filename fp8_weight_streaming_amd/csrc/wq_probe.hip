@@ -21,9 +21,12 @@ constexpr int kProbeUnroll = 8;
 
 // The read probe runs as the weight stream does: one workgroup of 8 waves
 // per CU, each wave streaming its own contiguous share of the buffer in
-// whole 1 KB requests (16 bytes per lane), 8 requests in flight.  (A grid of
-// many small workgroups striding over the whole buffer read about 10% slower
-// on MI355X.)
+// whole 1 KB requests (16 bytes per lane), 8 requests in flight as a ring
+// (each slot's next load issued as soon as its last one is consumed).  On
+// MI355X: a grid of many small workgroups striding over the whole buffer
+// read about 10% slower; batches of 8 loads consumed together 1.5% slower
+// than the ring; rings of 12 or 16 the same as 8 (7.0 TB/s); default-policy
+// loads 12% slower than non-temporal ones.
 constexpr int kReadThreads = 512;
 constexpr int kReadWaves = kReadThreads / 64;
 
@@ -46,14 +49,20 @@ __global__ __launch_bounds__(kReadThreads) void probe_read_kernel(const char* __
                                         0x00020000);
   const uint32_t steps = (uint32_t)((v1 - v0 + 63) / 64);
   uint32_t acc = 0, cursor = 0;
+  // (loads past the share read as zero, so the ring may run ahead of it)
+  auto load = [&](uint32_t step) {
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)((step * 64u + lane) * 16u), 0, 2 /* nt */));
+  };
+  u32x4 v[kProbeUnroll];
+#pragma unroll
+  for (int u = 0; u < kProbeUnroll; ++u) v[u] = load((uint32_t)u);
   for (uint32_t s = 0; s < steps; s += kProbeUnroll) {
-    u32x4 v[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u)
-      v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(((s + u) * 64u + lane) * 16u),
-                                                                            0, 2 /* nt */));
-#pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      v[u] = load(s + kProbeUnroll + (uint32_t)u);
+    }
     if (WRITE && (s + kProbeUnroll) % every == 0) {
       __builtin_amdgcn_raw_buffer_store_b32(acc, rd, (int)(cursor + 4u * lane), 0, 16 /* sc1 */);
       cursor += 256u;
@@ -77,8 +86,9 @@ wq_status read_geom(size_t bytes, ReadGeom* g) {
   g->grid = cus < 2048 ? cus : 2048;
   const uint64_t nw = (uint64_t)g->grid * kReadWaves;
   const uint64_t share = (bytes / 16 + nw - 1) / nw;  // 16-byte vectors of the longest share
-  // each wave's share is addressed with 32-bit offsets
-  if (share * 16 >= (1ull << 31)) return WQ_ERROR_UNSUPPORTED_SHAPE;
+  // each wave's share (and the ring's loads up to 8 KB past it) is
+  // addressed with 32-bit offsets
+  if (share * 16 + 16 * 1024 >= (1ull << 31)) return WQ_ERROR_UNSUPPORTED_SHAPE;
   g->wave_steps = ((share + 63) / 64 + kProbeUnroll - 1) / kProbeUnroll * kProbeUnroll;
   return WQ_SUCCESS;
 }
