@@ -36,6 +36,10 @@
 //    steps into one run per workgroup and one piece per wave; tiles whose K
 //    chunks end in different workgroups are finished by the last one to
 //    arrive (an arrival counter per tile), adding the parts in chunk order.
+//  * Output writes are what the stream pays for beyond its reads, and they
+//    cost least when the whole chip writes at once: from N = 4 up each wave
+//    holds its last pair of tiles' outputs until the chip-wide 100 MHz clock
+//    enters a new window (or its next tile ends), so that writes bunch.
 //
 // Numerics do not depend on N: a column's A rows, its MFMA sums, its FMA
 // rescale chain and its chunk sum are the same whatever the other columns
@@ -675,11 +679,12 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
   // two whole 128-byte lines, rows n and n + 4 of 32 consecutive m.  A tile
   // without its partner in the share is written alone, as half lines.
   //
-  // Every step issues the same min(N, 4) stores; only on a tile's last step
-  // do their offsets point into the buffer, otherwise the range check drops
-  // them.  An equal count of memory operations on every step keeps the
-  // compiler's vmcnt waits exact across the epilogue (a conditional store
-  // makes it wait for everything).
+  // Every step issues the same min(N, 4) stores; only on the step that
+  // writes a pair (the pair's last tile, or with deferred outputs the step
+  // that releases the held pair) do their offsets point into the buffer,
+  // otherwise the range check drops them.  An equal count of memory
+  // operations on every step keeps the compiler's vmcnt waits exact across
+  // the epilogue (a conditional store makes it wait for everything).
   constexpr int kStores = N < 4 ? N : 4;
   const bool blocked = BLK && ptile0 >= 0;
   const bool split = mt.nchunks > 1 && !blocked;
