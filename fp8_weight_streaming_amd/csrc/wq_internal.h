@@ -244,6 +244,8 @@ constexpr int kSplitChunksMax = 24;
 // Threads per workgroup of the split kernel, and steps in flight per lane.
 constexpr int kSplitThreads = 512;
 constexpr int kSplitPrefetch = 3;
+// Most output pairs a wave holds in LDS until the end of a short run.
+constexpr int kHoldMax = 8;
 // Tiled-stream outputs held until the chip-wide 100 MHz clock enters a new
 // window of 2^kDeferWindowBits ticks (10.24 us), from kDeferMinN columns up.
 // Measured over the dense 64-layer pass (us per pass at N = 2 / 4 / 8):

@@ -39,7 +39,9 @@
 //  * Output writes are what the stream pays for beyond its reads, and they
 //    cost least when the whole chip writes at once: from N = 4 up each wave
 //    holds its last pair of tiles' outputs until the chip-wide 100 MHz clock
-//    enters a new window (or its next tile ends), so that writes bunch.
+//    enters a new window (or its next tile ends), so that writes bunch; a
+//    run short enough for all its pairs to wait in the LDS past its X chunk
+//    (a single product's, a tail claim's) writes them at its end.
 //
 // Numerics do not depend on N: a column's A rows, its MFMA sums, its FMA
 // rescale chain and its chunk sum are the same whatever the other columns
@@ -715,6 +717,31 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
   uint32_t pso[4] = {kDropOffset, kDropOffset, kDropOffset, kDropOffset};
   bool pending = false;
   uint32_t pwin = 0;
+  // Held outputs (the 8-wave tiled kernels, N >= kDeferMinN): when every
+  // pair this wave emits in the run fits in its share of the LDS between
+  // the run's X chunk and the zero block, the pairs' sums wait there and are
+  // written after the run's last step, so that a short run's outputs (a
+  // single product's, a tail claim's) reach memory at its end rather than
+  // one pair at a time while the whole chip streams.  Slot j holds the j-th
+  // pair emitted ([r][lane] floats): the pair of the j-th odd tile of the
+  // run, or the run's last tile alone when that tile is even, so its
+  // offsets follow from j.  Long runs (the dense verify pass) keep the
+  // clock-window deferral.
+  constexpr bool kHoldable = (EPI == kEpiStore || EPI == kEpiArgmax) && PF == kPrefetchTiled && N >= kDeferMinN;
+  const int tlast = tile0 + cnt - 1;
+  const int nodd = ((tlast + 1) >> 1) - (tile0 >> 1);  // odd tiles: each ends a pair
+  const int npairs = nodd + ((tlast & 1) == 0 ? 1 : 0);
+  const uint32_t xend = (uint32_t)nst * (uint32_t)kStep * 2u * N;  // bytes of the staged X chunk
+  constexpr uint32_t kHoldSlot = 256u * kStores;
+  const int nwv = (int)(blockDim.x >> 6);
+  const int hslots =
+      kHoldable ? min(kHoldMax, (int)((kZeroOffset<N>() - min(xend, kZeroOffset<N>())) / nwv / kHoldSlot)) : 0;
+  const bool hold = kHoldable && !blocked && obase != nullptr && npairs <= hslots;
+  char* const hbase =
+      kHoldable ? lds + xend + (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) * hslots * kHoldSlot
+                : lds;
+  int hcount = 0;
+  bool emitted = false;
 
   // next step to compute: tile ci, step cst
   int ci = 0, cst = 0;
@@ -772,6 +799,7 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       const bool odd = (t & 1) != 0;
       // emit a pair (odd tile), or a lone even tile at the end of the share
       const bool emit = odd || ci == cnt - 1;
+      if constexpr (kHoldable) emitted = emit;
       // store lanes: n = r + 4 * (lane / 32), m = m0 + lane % 32, where
       // m % 32 < 16 comes from the even tile and the rest from the odd one
       const int m = 16 * (odd ? t - 1 : t) + (lane & 31);
@@ -825,32 +853,50 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
       }
       if (to_lds && lane < 32) *reinterpret_cast<f32x4*>(lds + poff) = pout;
     }
-    if constexpr (kDefer) {
-      // the same min(N, 4) stores on every step; real offsets only when the
-      // held pair is written (a new window, the end of a tile, or a new pair
-      // to hold)
-      const uint32_t win = (uint32_t)(__builtin_amdgcn_s_memrealtime() >> kDeferWindowBits);
-      const bool emit_now = fin && so[0] != kDropOffset;
-      const bool fl = pending && (win != pwin || fin);
+    bool held = false;
+    if constexpr (kHoldable) {
+      if (hold) {
+        // the same min(N, 4) stores on every step, all dropped; a finished
+        // pair goes to its slot
+        held = true;
 #pragma unroll
-      for (int r = 0; r < kStores; ++r) bstore4(psum[r], ro, fl ? pso[r] : kDropOffset + 4u * r);
-      if (fl) pending = false;
-      if (emit_now) {
+        for (int r = 0; r < kStores; ++r) bstore4(sum[r], ro, kDropOffset + 4u * r);
+        if (fin && emitted) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          psum[r] = sum[r];
-          pso[r] = so[r];
+          for (int r = 0; r < kStores; ++r)
+            *reinterpret_cast<float*>(hbase + (uint32_t)hcount * kHoldSlot + 256u * r + 4u * lane) = sum[r];
+          ++hcount;
         }
-        pending = true;
-        pwin = win;
       }
-    } else {
+    }
+    if (!held) {
+      if constexpr (kDefer) {
+        // the same min(N, 4) stores on every step; real offsets only when
+        // the held pair is written (a new window, the end of a tile, or a
+        // new pair to hold)
+        const uint32_t win = (uint32_t)(__builtin_amdgcn_s_memrealtime() >> kDeferWindowBits);
+        const bool emit_now = fin && so[0] != kDropOffset;
+        const bool fl = pending && (win != pwin || fin);
 #pragma unroll
-      for (int r = 0; r < kStores; ++r) {
-        if constexpr (EPI == kEpiGlu)
-          bstore2(sbits[r], ro, fin ? so[r] : kDropOffset);
-        else
-          bstore4(sum[r], ro, fin ? so[r] : kDropOffset);
+        for (int r = 0; r < kStores; ++r) bstore4(psum[r], ro, fl ? pso[r] : kDropOffset + 4u * r);
+        if (fl) pending = false;
+        if (emit_now) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            psum[r] = sum[r];
+            pso[r] = so[r];
+          }
+          pending = true;
+          pwin = win;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < kStores; ++r) {
+          if constexpr (EPI == kEpiGlu)
+            bstore2(sbits[r], ro, fin ? so[r] : kDropOffset);
+          else
+            bstore4(sum[r], ro, fin ? so[r] : kDropOffset);
+        }
       }
     }
     if (++cst == nst) { cst = 0; ++ci; }
@@ -890,6 +936,22 @@ __device__ void tiled_run(const DevMat& mt, int chunk, int64_t first, int64_t en
     if (pending) {
 #pragma unroll
       for (int r = 0; r < kStores; ++r) bstore4(psum[r], ro, pso[r]);
+    }
+  }
+  if (kHoldable && hold) {
+    // the held pairs, with the offsets the epilogue gives them
+    for (int j = 0; j < hcount; ++j) {
+      const bool podd = j < nodd;
+      const int t = podd ? (tile0 | 1) + 2 * j : tlast;
+      const int m = 16 * (podd ? t - 1 : t) + (lane & 31);
+      const bool half_ok = (lane & 16) ? podd : (!podd || t > tile0);
+#pragma unroll
+      for (int r = 0; r < kStores; ++r) {
+        const int n = r + 4 * (lane >> 5);
+        const bool live = half_ok && m < mt.M && n < N;
+        bstore4(*reinterpret_cast<const float*>(hbase + (uint32_t)j * kHoldSlot + 256u * r + 4u * lane), ro,
+                live ? (uint32_t)((n * mt.M + m) * 4) : kDropOffset);
+      }
     }
   }
 }

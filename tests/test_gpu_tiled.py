@@ -259,13 +259,39 @@ def test_mixed_pass_plain_and_tiled(wq):
         assert_close(m.y.cpu().numpy(), yr, ar, "mixed pass fmt=%d M=%d K=%d" % (m.fmt, m.M, m.K))
 
 
-def test_dynamic_tail_covers_every_unit_on_every_launch(wq):
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_short_runs_write_held_outputs(wq, fmt):
+    # Single tiled products with at least 8 row tiles per CU run the stream
+    # kernel, here with one or two tiles per wave: from N = 4 up each wave's
+    # output pairs wait in LDS until its run ends.  Ragged M (NVFP4: a last
+    # tile of one row at an even index, written alone; FP8: 15 rows at an
+    # odd index) and ragged K.  Every output (reset to NaN) must match the
+    # oracle, and each column the N = 1 product (whose outputs are written as
+    # they come) bit for bit.
+    if fmt == "nvfp4":
+        d = inputs.nvfp4_inputs(36001, 544, 8, seed=2100, g=0.02)
+        run = run_tiled
+        yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x)
+    else:
+        d = inputs.fp8row_inputs(35999, 272, 8, seed=2101)
+        run = run_fp8_tiled
+        yr, ar = oracle.gemm_fp8row(d.w, d.row_scale, d.x)
+    y1 = run(wq, d, 1)
+    for N in (4, 5, 8):
+        print("held outputs %s M=%d K=%d N=%d" % (fmt, d.M, d.K, N), flush=True)
+        y = run(wq, d, N)
+        assert_close(y, yr[:N], ar[:N], "held outputs %s N=%d" % (fmt, N))
+        assert np.array_equal(y[:1].view(np.uint32), y1.view(np.uint32)), "column 0 differs from N = 1, N=%d" % N
+
+
+@pytest.mark.parametrize("N", [3, 8])
+def test_dynamic_tail_covers_every_unit_on_every_launch(wq, N):
     # A pass large enough (>= 256 units per workgroup) for the dynamic tail:
     # two tiled matrices, so the tail crosses a matrix boundary.  Every output
     # of every one of three launches (outputs reset to NaN in between) must
     # match the oracle: a chunk claimed twice or never would show, and so
-    # would a counter not reset for the next launch.
-    N = 3
+    # would a counter not reset for the next launch.  (At N = 8 the tail
+    # claims' outputs wait in LDS until each claim ends.)
     specs = [(600000, 256), (500000, 256)]
     host = [inputs.nvfp4_inputs(M, K, N, seed=1900 + i, g=0.02) for i, (M, K) in enumerate(specs)]
     mats = []
@@ -279,7 +305,7 @@ def test_dynamic_tail_covers_every_unit_on_every_launch(wq):
     for launch in range(3):
         for m in mats:
             m.y.fill_(float("nan"))
-        print("tail launch %d" % launch, flush=True)
+        print("tail launch %d N=%d" % (launch, N), flush=True)
         wq.wq_verify_launch(plan)
         torch.cuda.synchronize()
         for m, (yr, ar) in zip(mats, refs):
