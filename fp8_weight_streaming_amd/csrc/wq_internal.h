@@ -143,10 +143,13 @@ struct WgRange {
 // The dynamic tail of a verify pass, stored right after the grid + 1
 // ranges: units [begin, end) are handed out as `count` claims, in order, to
 // whichever workgroup asks next (an atomic counter), so that workgroups
-// that streamed their static range faster take more.  `next` and `done`
-// start at 0 (the plan's upload zeroes them); the last workgroup to finish a
-// launch sets them back to 0.  The claims follow (count + 1 entries, the
-// last one only ending the one before): claim i is units
+// that streamed their static range faster take more.  `next` starts at 0
+// (the plan's upload zeroes it) and only grows: a launch takes every claim
+// once and each workgroup one value past the last claim (the one that ends
+// its loop), count + grid values in all, so launch L's claims are
+// L (count + grid) + i and nothing is reset between launches.  A plan
+// without a tail (count 0) takes no claims.  The claims follow (count + 1
+// entries, the last one only ending the one before): claim i is units
 // [claims[i].begin, claims[i + 1].begin), whose first unit is in matrix
 // claims[i].mat.
 struct DynSched {
@@ -154,8 +157,7 @@ struct DynSched {
   int64_t end;
   int32_t chunk;  // units per claim outside blocked matrices
   int32_t count;
-  uint32_t next;
-  uint32_t done;
+  uint64_t next;
 };
 struct DynClaim {
   int64_t begin;

@@ -1433,9 +1433,12 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
   // the dynamic tail until none is left
   // (only the tiled kernel has the claim loop: plans of other kernels have no
   // tail, and the loop's presence alone slowed the plain-layout kernels)
-  DynSched* const dyn = ((MODE == kModeTiled || MODE == kModeTiledValu) && mats)
-                            ? reinterpret_cast<DynSched*>(const_cast<WgRange*>(ranges) + gridDim.x + 1)
-                            : nullptr;
+  DynSched* dyn = ((MODE == kModeTiled || MODE == kModeTiledValu) && mats)
+                      ? reinterpret_cast<DynSched*>(const_cast<WgRange*>(ranges) + gridDim.x + 1)
+                      : nullptr;
+  // a pass without a tail takes no claims (a claim is a device-scope round
+  // trip that the last workgroup's exit would wait for)
+  if (dyn && dyn->count == 0) dyn = nullptr;
   __shared__ uint32_t s_claim;
   bool waited = false;
   int bchunk = 0;  // blocked split: the next chunk of the current block
@@ -1599,7 +1602,11 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
   }
   if (!dyn) break;
   __syncthreads();  // every wave has read the previous claim
-  if (threadIdx.x == 0) s_claim = atomicAdd(&dyn->next, 1u);
+  if (threadIdx.x == 0) {
+    // this launch's values of the counter are L (count + grid) + i
+    const uint64_t raw = __hip_atomic_fetch_add(&dyn->next, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_claim = (uint32_t)(raw % ((uint64_t)dyn->count + gridDim.x));
+  }
   __syncthreads();
   const uint32_t idx = s_claim;
   if (idx >= (uint32_t)dyn->count) break;
@@ -1610,13 +1617,6 @@ __device__ __forceinline__ void stream_body(const DevMat* __restrict__ mats, con
   }
   if constexpr (SYNC) {
     if (!waited) grid_wait(*gs);
-  }
-  // The last workgroup to finish sets the counters back for the next launch.
-  // Every workgroup's final claim has returned before its `done` increment
-  // (its exit depends on the claim's value), so no claim can follow.
-  if (dyn && threadIdx.x == 0 && atomicAdd(&dyn->done, 1u) == gridDim.x - 1) {
-    atomicExch(&dyn->next, 0u);
-    atomicExch(&dyn->done, 0u);
   }
 
   if constexpr (MODE == kModeTiledArgmax) {
