@@ -245,7 +245,11 @@ wq_status wq_verify_pass(const wq_matrix* descs, int count, int N,
  * `stream`), filling `plan`; wq_verify_launch then only launches the
  * kernel and can be called any number of times, on any stream ordered
  * after the copy, for as long as the workspace and every matrix buffer
- * stay alive and unchanged in place.  wq_verify_pass is prepare + launch.
+ * stay alive and unchanged in place (apart from the claim counter of the
+ * pass's dynamic tail, which each launch advances and none resets).
+ * Launches of one plan share that counter: they must run one after
+ * another (one stream, or ordered by events), never at the same time.
+ * wq_verify_pass is prepare + launch.
  * The plan's fields are owned by the library; callers only keep it
  * (reduce_runs: reduction blocks launched after the pass, 0 when there are
  * none; lds_extra: LDS bytes per workgroup for blocked chunk sums). */
