@@ -125,6 +125,58 @@ def fp8row_inputs(M: int, K: int, N: int, seed: int) -> FP8RowInputs:
     return FP8RowInputs(w=w, row_scale=r, x=x)
 
 
+# ---- hashed rows: matrices too large to draw ------------------------------
+# The largest matrices the tiled layouts address hold just under 2**32 bytes;
+# drawing all their weights from PCG64 on the host takes tens of GB of
+# temporaries.  These functions give any chosen rows of such a matrix
+# instead, from a closed-form hash of (seed, row, column): a test builds the
+# matrix on the device chunk by chunk and hands the oracle only the rows it
+# checks.  Every row differs from every other, so a tile read from the wrong
+# place shows.  Byte (m, j) is the top byte of h(m) * h'(j) (mod 2**32), with
+# h and h' xorshift-multiply mixes of the row and column indices and h'
+# forced odd: two rows a, b then differ by (h(a) - h(b)) * h'(j) in column
+# j, which reaches the top byte for nearly every j.
+
+def _mix32(a: np.ndarray, seed: int) -> np.ndarray:
+    """xorshift-multiply mix of uint32 values (a fixed bijection per seed)."""
+    a = (np.asarray(a, dtype=np.uint64) ^ np.uint64(seed & 0xFFFFFFFF)) & np.uint64(0xFFFFFFFF)
+    for mul in (0x9E3779B1, 0x85EBCA6B, 0xC2B2AE35):
+        a = (a ^ (a >> np.uint64(15))) * np.uint64(mul) & np.uint64(0xFFFFFFFF)
+    return (a ^ (a >> np.uint64(16))).astype(np.uint32)
+
+
+def _hashed_bytes(rows: np.ndarray, cols: int, seed: int) -> np.ndarray:
+    """uint8 [len(rows), cols]: the top byte of h(row) * h'(col) mod 2**32."""
+    hr = _mix32(np.asarray(rows, dtype=np.uint64), seed)[:, None]
+    hc = (_mix32(np.arange(cols, dtype=np.uint64), seed ^ 0x5A5A5A5A) | np.uint32(1))[None, :]
+    return ((hr * hc) >> np.uint32(24)).astype(np.uint8)
+
+
+# E4M3 block scales of the hashed matrices: 2**e and 1.5 * 2**e, e in [-4, 3]
+_HASHED_SCALES = np.array([((e + 7) << 3) | m for e in range(-4, 4) for m in (0, 4)], dtype=np.uint8)
+
+
+def hashed_nvfp4_rows(rows: np.ndarray, K: int, seed: int):
+    """Rows `rows` of a hashed NVFP4 matrix with K columns: (codes uint8
+    [len(rows), K/2], uniform-looking bytes; scales uint8 [len(rows), K/16]
+    from the 16 table values above)."""
+    if K % 32:
+        raise ValueError("NVFP4 K must be a multiple of 32")
+    codes = _hashed_bytes(rows, K // 2, seed)
+    scales = _HASHED_SCALES[_hashed_bytes(rows, K // 16, seed + 1) >> 4]
+    return codes, scales
+
+
+def hashed_fp8_rows(rows: np.ndarray, K: int, seed: int):
+    """Rows `rows` of a hashed row-scaled FP8-E4M3 matrix: (w uint8
+    [len(rows), K], bytes with the lowest exponent bit cleared, so no NaN
+    code; row_scale float32 [len(rows)], 2**-10 * (1 + j / 8), j in 0..7)."""
+    w = _hashed_bytes(rows, K, seed) & np.uint8(0xF7)
+    j = _mix32(np.asarray(rows, dtype=np.uint64), seed + 2) >> np.uint32(29)
+    r = (np.float32(2.0 ** -10) * (np.float32(1.0) + j.astype(np.float32) / np.float32(8.0))).astype(np.float32)
+    return w, r
+
+
 # ---- the five workloads --------------------------------------------------
 
 @dataclass
