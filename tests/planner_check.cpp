@@ -16,6 +16,10 @@
 #include <cstdio>
 #include <random>
 
+// The dynamic tail's 64-bit claim counter is 8-byte aligned in the
+// workspace: DynSched follows the 16-byte WgRange entries.
+static_assert(sizeof(wq::WgRange) == 16 && offsetof(wq::DynSched, next) % 8 == 0, "claim counter alignment");
+
 using namespace wq;
 
 struct Seg {

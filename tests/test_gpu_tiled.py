@@ -290,8 +290,11 @@ def test_dynamic_tail_covers_every_unit_on_every_launch(wq, N):
     # two tiled matrices, so the tail crosses a matrix boundary.  Every output
     # of every one of three launches (outputs reset to NaN in between) must
     # match the oracle: a chunk claimed twice or never would show, and so
-    # would a counter not reset for the next launch.  (At N = 8 the tail
-    # claims' outputs wait in LDS until each claim ends.)
+    # would a claim counter that left a launch in the wrong state for the
+    # next.  Then the plan is prepared again into the same workspace (the
+    # counter starts over at zero) and two more launches must give the same
+    # bits.  (At N = 8 the tail claims' outputs wait in LDS until each claim
+    # ends.)
     specs = [(600000, 256), (500000, 256)]
     host = [inputs.nvfp4_inputs(M, K, N, seed=1900 + i, g=0.02) for i, (M, K) in enumerate(specs)]
     mats = []
@@ -310,6 +313,16 @@ def test_dynamic_tail_covers_every_unit_on_every_launch(wq, N):
         torch.cuda.synchronize()
         for m, (yr, ar) in zip(mats, refs):
             assert_close(m.y.cpu().numpy(), yr, ar, "launch %d M=%d" % (launch, m.M))
+    last = [m.y.clone() for m in mats]
+    plan = wq.wq_verify_prepare(mats, N, ws)
+    for launch in range(2):
+        for m in mats:
+            m.y.fill_(float("nan"))
+        print("tail launch %d after a new prepare N=%d" % (launch, N), flush=True)
+        wq.wq_verify_launch(plan)
+        torch.cuda.synchronize()
+        for m, y0 in zip(mats, last):
+            assert torch.equal(m.y.view(torch.int32), y0.view(torch.int32)), "after a new prepare M=%d" % m.M
 
 
 def test_blocked_split_pass(wq):
