@@ -259,7 +259,7 @@ def test_mixed_pass_plain_and_tiled(wq):
         assert_close(m.y.cpu().numpy(), yr, ar, "mixed pass fmt=%d M=%d K=%d" % (m.fmt, m.M, m.K))
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8", "nvfp4-ksplit"])
 def test_short_runs_write_held_outputs(wq, fmt):
     # Single tiled products with at least 8 row tiles per CU run the stream
     # kernel, here with one or two tiles per wave: from N = 4 up each wave's
@@ -267,8 +267,14 @@ def test_short_runs_write_held_outputs(wq, fmt):
     # tile of one row at an even index, written alone; FP8: 15 rows at an
     # odd index) and ragged K.  Every output (reset to NaN) must match the
     # oracle, and each column the N = 1 product (whose outputs are written as
-    # they come) bit for bit.
-    if fmt == "nvfp4":
+    # they come) bit for bit.  nvfp4-ksplit: K = 10240 in two chunks of 5120,
+    # so the held pairs are chunk sums written to the partial planes that a
+    # reduction then adds.
+    if fmt == "nvfp4-ksplit":
+        d = inputs.nvfp4_inputs(36001, 10240, 8, seed=2102, g=0.02)
+        run = run_tiled
+        yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x)
+    elif fmt == "nvfp4":
         d = inputs.nvfp4_inputs(36001, 544, 8, seed=2100, g=0.02)
         run = run_tiled
         yr, ar = oracle.gemm_nvfp4(d.codes, d.scales, d.g, d.x)
