@@ -27,9 +27,11 @@ def tiled_of(wq, d):
 
 
 def test_noalloc_matches_workspace_call_twice(wq):
-    # the down-projection shape at N = 8, then a smaller split shape at N = 3
-    # with a ragged last tile and chunk
-    cases = [(5120, 17408, 8, 2101), (1000, 8736, 3, 2102)]
+    # a product with many tiles per CU (the chunked stream kernel, its chunk
+    # sums in the scratch for a reduction, its outputs held in LDS), the
+    # down-projection shape at N = 8 (split across workgroups), then a
+    # smaller split shape at N = 3 with a ragged last tile and chunk
+    cases = [(36001, 10240, 8, 2100), (5120, 17408, 8, 2101), (1000, 8736, 3, 2102)]
     for M, K, N, seed in cases:
         need = wq.wq_gemm_workspace_bytes(wq.WQ_FMT_NVFP4_TILED, M, K, N)
         print("noalloc case M=%d K=%d N=%d scratch %d bytes" % (M, K, N, need), flush=True)
